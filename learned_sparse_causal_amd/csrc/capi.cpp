@@ -1,0 +1,263 @@
+// Host side of the C ABI declared in include/mono.h: argument validation,
+// workspace layout and kernel dispatch.  Every entry point validates on the
+// host before enqueueing anything; nothing here allocates, frees or
+// synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "common.hpp"
+#include "mono.h"
+
+hipError_t launch_block_address(const Shape &s, const void *k, const float *cos_t,
+                                const float *sin_t, const float *cb, float *kbar, int32_t *addr,
+                                hipStream_t st);
+hipError_t launch_posting_lists(const Shape &s, const int32_t *addr, int32_t *offsets,
+                                int32_t *entries, int32_t *load, int32_t *overflow, hipStream_t st);
+hipError_t launch_index_stats(const Shape &s, const int32_t *overflow, const int32_t *load,
+                              int32_t *stats, hipStream_t st);
+hipError_t launch_route(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
+                        const float *cb, const float *kbar, const int32_t *addr,
+                        const int32_t *offsets, const int32_t *entries, const int32_t *load,
+                        int32_t *sel, hipStream_t st);
+size_t attention_ws_layout(const Shape &s, size_t *off);
+hipError_t launch_attention(const Shape &s, const void *q, const void *k, const void *v,
+                            const float *cos_t, const float *sin_t, const int32_t *sel, void *out,
+                            void *ws, hipStream_t st);
+hipError_t launch_gemm(int bf16, int M, int N, int Kd, const void *A, const void *Bm, void *C,
+                       hipStream_t st);
+hipError_t launch_gemm_qkv(int bf16, int M, int N, int Kd, const void *A, const void *Bm, void *q,
+                           void *k, void *v, int nq, int nk, hipStream_t st);
+
+namespace {
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+mono_status make_shape(const mono_config *c, bool mixer, Shape &s) {
+    if (!c) return MONO_ERR_NULL;
+    const int32_t pos[] = {c->batch, c->seq_len, c->n_q_heads, c->n_kv_heads, c->head_dim,
+                           c->block_size, c->n_components, c->codes_per_component, c->capacity,
+                           c->n_probes, c->n_remote, c->n_local};
+    for (int32_t x : pos)
+        if (x < 1) return MONO_ERR_SHAPE;
+    if (mixer && c->width < 1) return MONO_ERR_SHAPE;
+    if (c->seq_len % c->block_size) return MONO_ERR_SHAPE;
+    if (c->head_dim % c->n_components) return MONO_ERR_SHAPE;
+    if (c->n_q_heads % c->n_kv_heads) return MONO_ERR_SHAPE;
+    if (mixer && c->n_q_heads * c->head_dim != c->width) return MONO_ERR_SHAPE;
+    if (c->dtype != MONO_F32 && c->dtype != MONO_BF16) return MONO_ERR_UNSUPPORTED;
+    if (c->head_dim != 64 && c->head_dim != 128) return MONO_ERR_UNSUPPORTED;
+    if (c->block_size != 64 && c->block_size != 128) return MONO_ERR_UNSUPPORTED;
+    if (c->n_components != 1 && c->n_components != 2) return MONO_ERR_UNSUPPORTED;
+    if (c->codes_per_component < 2 || c->codes_per_component > 64) return MONO_ERR_UNSUPPORTED;
+    if (c->n_probes > 16) return MONO_ERR_UNSUPPORTED;
+    const int NB = c->seq_len / c->block_size;
+    if (NB > 8192) return MONO_ERR_UNSUPPORTED;
+    if (c->n_remote > 16 && NB - c->n_local > c->n_remote) return MONO_ERR_UNSUPPORTED;
+    const double routes = (double)c->batch * c->n_q_heads * c->seq_len;
+    if (routes * c->n_remote >= 2147483647.0) return MONO_ERR_UNSUPPORTED;
+    if (mixer && c->width % 8) return MONO_ERR_UNSUPPORTED;
+    s.B = c->batch;
+    s.T = c->seq_len;
+    s.W = c->width;
+    s.Hq = c->n_q_heads;
+    s.Hkv = c->n_kv_heads;
+    s.d = c->head_dim;
+    s.beta = c->block_size;
+    s.P = c->n_components;
+    s.K = c->codes_per_component;
+    s.cap = c->capacity;
+    s.npr = c->n_probes;
+    s.R = c->n_remote;
+    s.L = c->n_local;
+    s.dtype = c->dtype;
+    s.NB = NB;
+    s.A = 1;
+    for (int p = 0; p < s.P; ++p) s.A *= s.K;
+    s.G = s.Hq / s.Hkv;
+    s.ds = s.d / s.P;
+    return MONO_OK;
+}
+
+size_t esize(const Shape &s) { return s.dtype == MONO_BF16 ? 2 : 4; }
+
+// Mixer workspace: q, k, v, kbar, addr, offsets, entries, load, overflow,
+// sel, attention output, inner workspace.
+size_t mixer_layout(const Shape &s, size_t *off) {
+    const size_t es = esize(s);
+    const size_t BT = (size_t)s.B * s.T;
+    const size_t BG = (size_t)s.B * s.Hkv;
+    size_t p = 0;
+    off[0] = p; p = al256(p + BT * s.Hq * s.d * es);
+    off[1] = p; p = al256(p + BT * s.Hkv * s.d * es);
+    off[2] = p; p = al256(p + BT * s.Hkv * s.d * es);
+    off[3] = p; p = al256(p + BG * s.NB * s.d * 4);
+    off[4] = p; p = al256(p + BG * s.NB * 4);
+    off[5] = p; p = al256(p + BG * (s.A + 1) * 4);
+    off[6] = p; p = al256(p + BG * s.NB * 4);
+    off[7] = p; p = al256(p + BG * s.A * 4);
+    off[8] = p; p = al256(p + BG * 4);
+    off[9] = p; p = al256(p + BT * s.Hq * s.R * 4);
+    off[10] = p; p = al256(p + BT * s.Hq * s.d * es);
+    off[11] = p;
+    size_t aoff[9];
+    p += attention_ws_layout(s, aoff);
+    return p;
+}
+
+mono_status hip_status(hipError_t e) { return e == hipSuccess ? MONO_OK : MONO_ERR_HIP; }
+
+bool index_ok(const mono_index *x) {
+    return x && x->kbar && x->addr && x->offsets && x->entries && x->load && x->overflow;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mono_workspace_bytes(const mono_config *cfg, int which) {
+    Shape s;
+    const bool mixer = which == MONO_WS_MIXER;
+    if (make_shape(cfg, mixer, s) != MONO_OK) return 0;
+    size_t off[12];
+    switch (which) {
+        case MONO_WS_BUILD:
+        case MONO_WS_ROUTE:
+            return 0;
+        case MONO_WS_ATTENTION:
+            return attention_ws_layout(s, off);
+        case MONO_WS_MIXER:
+            return mixer_layout(s, off);
+        default:
+            return 0;
+    }
+}
+
+mono_status mono_rope_table(int32_t seq_len, int32_t head_dim, double base, float *cos_tab,
+                            float *sin_tab) {
+    if (!cos_tab || !sin_tab) return MONO_ERR_NULL;
+    if (seq_len < 1 || head_dim < 2 || head_dim % 2 || !(base > 0.0)) return MONO_ERR_SHAPE;
+    const int h = head_dim / 2;
+    for (int i = 0; i < h; ++i) {
+        const double inv_freq = std::pow(base, -(2.0 * (double)i) / (double)head_dim);
+        for (int t = 0; t < seq_len; ++t) {
+            const double ang = (double)t * inv_freq;
+            cos_tab[(size_t)t * h + i] = (float)std::cos(ang);
+            sin_tab[(size_t)t * h + i] = (float)std::sin(ang);
+        }
+    }
+    return MONO_OK;
+}
+
+mono_status mono_build_index(const mono_config *cfg, const void *k, const float *rope_cos,
+                             const float *rope_sin, const float *codebooks, const mono_index *out,
+                             void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!k || !rope_cos || !rope_sin || !codebooks || !index_ok(out)) return MONO_ERR_NULL;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = launch_block_address(s, k, rope_cos, rope_sin, codebooks, out->kbar, out->addr, hs);
+    if (e != hipSuccess) return MONO_ERR_HIP;
+    e = launch_posting_lists(s, out->addr, out->offsets, out->entries, out->load, out->overflow, hs);
+    return hip_status(e);
+}
+
+mono_status mono_route(const mono_config *cfg, const void *q, const float *rope_cos,
+                       const float *rope_sin, const float *codebooks, const mono_index *idx,
+                       int32_t *sel, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!q || !rope_cos || !rope_sin || !codebooks || !index_ok(idx) || !sel) return MONO_ERR_NULL;
+    return hip_status(launch_route(s, q, rope_cos, rope_sin, codebooks, idx->kbar, idx->addr,
+                                   idx->offsets, idx->entries, idx->load, sel,
+                                   reinterpret_cast<hipStream_t>(stream)));
+}
+
+mono_status mono_selected_attention(const mono_config *cfg, const void *q, const void *k,
+                                    const void *v, const float *rope_cos, const float *rope_sin,
+                                    const int32_t *sel, void *out, void *ws, size_t ws_bytes,
+                                    void *stream) {
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!q || !k || !v || !rope_cos || !rope_sin || !sel || !out || !ws) return MONO_ERR_NULL;
+    size_t off[9];
+    if (ws_bytes < attention_ws_layout(s, off)) return MONO_ERR_WORKSPACE;
+    return hip_status(launch_attention(s, q, k, v, rope_cos, rope_sin, sel, out, ws,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+mono_status mono_mixer_layout(const mono_config *cfg, size_t *offsets_out) {
+    if (!offsets_out) return MONO_ERR_NULL;
+    Shape s;
+    const mono_status st = make_shape(cfg, true, s);
+    if (st != MONO_OK) return st;
+    mixer_layout(s, offsets_out);
+    return MONO_OK;
+}
+
+mono_status mono_mixer_forward(const mono_config *cfg, const void *x, const void *w_qkv,
+                               const void *w_o, const float *codebooks, const float *rope_cos,
+                               const float *rope_sin, void *delta, int32_t *stats, void *ws,
+                               size_t ws_bytes, void *stream) {
+    Shape s;
+    const mono_status st = make_shape(cfg, true, s);
+    if (st != MONO_OK) return st;
+    if (!x || !w_qkv || !w_o || !codebooks || !rope_cos || !rope_sin || !delta || !ws)
+        return MONO_ERR_NULL;
+    size_t off[12];
+    if (ws_bytes < mixer_layout(s, off)) return MONO_ERR_WORKSPACE;
+    unsigned char *base = reinterpret_cast<unsigned char *>(ws);
+    void *q = base + off[0], *k = base + off[1], *v = base + off[2];
+    mono_index idx;
+    idx.kbar = reinterpret_cast<float *>(base + off[3]);
+    idx.addr = reinterpret_cast<int32_t *>(base + off[4]);
+    idx.offsets = reinterpret_cast<int32_t *>(base + off[5]);
+    idx.entries = reinterpret_cast<int32_t *>(base + off[6]);
+    idx.load = reinterpret_cast<int32_t *>(base + off[7]);
+    idx.overflow = reinterpret_cast<int32_t *>(base + off[8]);
+    int32_t *sel = reinterpret_cast<int32_t *>(base + off[9]);
+    void *attn = base + off[10];
+    void *inner = base + off[11];
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const int bf = s.dtype == MONO_BF16;
+    const int M = s.B * s.T;
+    const int nq = s.Hq * s.d, nk = s.Hkv * s.d;
+    if (launch_gemm_qkv(bf, M, nq + 2 * nk, s.W, x, w_qkv, q, k, v, nq, nk, hs) != hipSuccess)
+        return MONO_ERR_HIP;
+    if (launch_block_address(s, k, rope_cos, rope_sin, codebooks, idx.kbar, idx.addr, hs) !=
+        hipSuccess)
+        return MONO_ERR_HIP;
+    if (launch_posting_lists(s, idx.addr, idx.offsets, idx.entries, idx.load, idx.overflow, hs) !=
+        hipSuccess)
+        return MONO_ERR_HIP;
+    if (stats && launch_index_stats(s, idx.overflow, idx.load, stats, hs) != hipSuccess)
+        return MONO_ERR_HIP;
+    if (launch_route(s, q, rope_cos, rope_sin, codebooks, idx.kbar, idx.addr, idx.offsets,
+                     idx.entries, idx.load, sel, hs) != hipSuccess)
+        return MONO_ERR_HIP;
+    if (launch_attention(s, q, k, v, rope_cos, rope_sin, sel, attn, inner, hs) != hipSuccess)
+        return MONO_ERR_HIP;
+    return hip_status(launch_gemm(bf, M, s.W, nq, attn, w_o, delta, hs));
+}
+
+const char *mono_status_string(mono_status status) {
+    switch (status) {
+        case MONO_OK: return "ok";
+        case MONO_ERR_NULL: return "a required pointer is NULL";
+        case MONO_ERR_SHAPE: return "inconsistent sizes";
+        case MONO_ERR_UNSUPPORTED: return "shape or dtype outside the supported set";
+        case MONO_ERR_WORKSPACE: return "workspace too small";
+        case MONO_ERR_HIP: return "a HIP launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

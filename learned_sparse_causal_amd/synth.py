@@ -99,8 +99,16 @@ def random_selection(cfg: Config, seed, drop_prob=0.1):
         if E == 0:
             continue
         take = min(R, E)
-        keys = rng.random((B, Hq, beta, E))
-        pick = np.sort(np.argsort(keys, axis=-1)[..., :take], axis=-1).astype(np.int32)
+        if E > 8 * R:
+            # draws with replacement; a repeated block becomes an empty slot
+            pick = np.sort(rng.integers(0, E, (B, Hq, beta, R)), axis=-1)
+            dup = np.zeros(pick.shape, bool)
+            dup[..., 1:] = pick[..., 1:] == pick[..., :-1]
+            pick = np.sort(np.where(dup, np.iinfo(np.int32).max, pick), axis=-1)
+            pick = np.where(pick == np.iinfo(np.int32).max, -1, pick).astype(np.int32)
+        else:
+            keys = rng.random((B, Hq, beta, E))
+            pick = np.sort(np.argsort(keys, axis=-1)[..., :take], axis=-1).astype(np.int32)
         sel[:, :, qb * beta:(qb + 1) * beta, :take] = pick
     drop = rng.random((B, Hq, T)) < drop_prob
     nvalid = (sel >= 0).sum(-1)

@@ -1,0 +1,110 @@
+"""GPU routing (mono_route) against the oracle: selected block ids bit for
+bit, with near-ties (oracle score gap < 1e-5 relative) counted and excused,
+plus the stated invariants on every GPU selection."""
+import numpy as np
+import pytest
+
+from learned_sparse_causal_amd import binding, configs, synth
+from parity import (check_sel_invariants, compare_index, compare_sel, dev, host, index_to_host,
+                    sample_routes, say, small_inputs, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(cfg, q_dev, k_dev, codebooks):
+    t = torch()
+    cos, sin = binding.device_rope(cfg)
+    cb = t.from_numpy(codebooks).cuda()
+    idx = binding.build_index(cfg, k_dev, cos, sin, cb)
+    sel = binding.route(cfg, q_dev, cos, sin, cb, idx)
+    t.cuda.synchronize()
+    return index_to_host(idx), host(sel)
+
+
+def run_oracle(orc, cfg, q, k, codebooks, route_ids=None):
+    c, s = orc.rope_table(cfg.T, cfg.d)
+    sh = orc.Shape.of(**cfg.shape_kw())
+    idx = orc.build_index(sh, k, c, s, codebooks)
+    sel, gaps = orc.route(sh, q, c, s, codebooks, idx, route_ids)
+    return idx, sel, gaps
+
+
+CFGS = [configs.TINY, configs.SMALL, configs.ALL_ELIGIBLE, configs.sweep(4096),
+        configs.sweep(8192),
+        configs.SMALL.with_(name="P1_K64", P=1, K=64, Hq=4, Hkv=2),
+        configs.SMALL.with_(name="probes1_R1", n_probes=1, R=1, Hq=2, Hkv=2),
+        configs.SMALL.with_(name="probes16_R16_L3", n_probes=16, R=16, L=3, Hq=2, Hkv=1),
+        configs.SMALL.with_(name="probes8_R3_K5", n_probes=8, R=3, K=5, Hq=2, Hkv=2),
+        configs.SMALL.with_(name="d128_beta128_f32", d=128, beta=128, T=8192, Hq=2, Hkv=1,
+                            dtype="f32", n_probes=8, R=8),
+        configs.SMALL.with_(name="cap1", cap=1, Hq=4, Hkv=4)]
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
+def test_route_parity(orc, cfg):
+    say("[route] %s" % cfg.name)
+    inp, d = small_inputs(cfg)
+    g_idx, g_sel = run_gpu(cfg, d["q"], d["k"], inp["codebooks"])
+    o_idx, o_sel, gaps = run_oracle(orc, cfg, inp["q"], inp["k"], inp["codebooks"])
+    bad = compare_index(cfg, g_idx, o_idx)
+    check_sel_invariants(cfg, g_sel, g_idx)
+    n = compare_sel(cfg, g_sel, o_sel, gaps, bad)
+    say("  excused routes: %d of %d" % (n, cfg.routes))
+
+
+def test_route_parity_32k_sampled(orc):
+    cfg = configs.SWEEP_32K
+    say("[route] %s sampled" % cfg.name)
+    inp, d = small_inputs(cfg)
+    g_idx, g_sel = run_gpu(cfg, d["q"], d["k"], inp["codebooks"])
+    ids = sample_routes(cfg, 30000, seed=1, must=[(0, 0), (0, 15)])
+    o_idx, o_sel, gaps = run_oracle(orc, cfg, inp["q"], inp["k"], inp["codebooks"], ids)
+    bad = compare_index(cfg, g_idx, o_idx)
+    check_sel_invariants(cfg, g_sel, g_idx)
+    n = compare_sel(cfg, g_sel, o_sel, gaps, bad, route_ids=ids)
+    say("  excused routes: %d of %d sampled" % (n, len(ids)))
+
+
+def test_route_parity_large_sampled(orc):
+    """Largest workload: the whole index, and routes of the (b, h) pairs
+    (0, 0) and (7, 15) plus random routes (sampled scalar parity)."""
+    cfg = configs.LARGE
+    say("[route] %s sampled" % cfg.name)
+    d = synth.qkv_device(cfg)
+    g_idx, g_sel = run_gpu(cfg, d["q"], d["k"], d["codebooks"])
+    ids = sample_routes(cfg, 30000, seed=2, must=[(0, 0), (7, 15)])
+    q_h = host(d["q"])
+    o_idx, o_sel, gaps = run_oracle(orc, cfg, q_h, host(d["k"]), d["codebooks"], ids)
+    del q_h
+    bad = compare_index(cfg, g_idx, o_idx)
+    check_sel_invariants(cfg, g_sel, g_idx)
+    n = compare_sel(cfg, g_sel, o_sel, gaps, bad, route_ids=ids)
+    say("  excused routes: %d of %d sampled; overflow %d, max load %d" % (
+        n, len(ids), g_idx["overflow"].sum(), g_idx["load"].max()))
+
+
+def test_route_with_overflowed_eligible_blocks(orc):
+    """Every block on one address, capacity 1: searched queries see one indexed
+    block and pad the rest with -1; bypassed queries take every eligible block."""
+    cfg = configs.SMALL.with_(name="one_address_cap1", cap=1, R=2, L=1, Hq=2, Hkv=2)
+    say("[route] %s" % cfg.name)
+    k, cb = synth.stress_keys(cfg, "one_address")
+    inp = synth.qkv(cfg)
+    g_idx, g_sel = run_gpu(cfg, dev(inp["q"], cfg.dtype), dev(k, cfg.dtype), cb)
+    o_idx, o_sel, gaps = run_oracle(orc, cfg, inp["q"], k, cb)
+    compare_index(cfg, g_idx, o_idx, excuse=False)
+    assert np.array_equal(g_sel.reshape(-1, cfg.R), o_sel)
+    t = np.arange(cfg.T)
+    searched = (t // cfg.beta - cfg.L + 1) > cfg.R
+    assert (g_sel[:, :, searched] == np.array([0, -1])).all()
+
+
+def test_route_deterministic():
+    cfg = configs.sweep(8192)
+    say("[route] determinism %s" % cfg.name)
+    inp, d = small_inputs(cfg)
+    a = run_gpu(cfg, d["q"], d["k"], inp["codebooks"])
+    b = run_gpu(cfg, d["q"], d["k"], inp["codebooks"])
+    for k in a[0]:
+        assert np.array_equal(a[0][k], b[0][k]), k
+    assert np.array_equal(a[1], b[1])
