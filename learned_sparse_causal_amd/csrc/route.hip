@@ -10,39 +10,62 @@
 //
 // One lane owns one query (route); one wave owns 64 consecutive tokens of one
 // (batch, q-head), which all lie in one query block, so the query block, the
-// eligible range and every loop over blocks are wave-uniform.
+// eligible range and every loop over blocks are wave-uniform.  A workgroup's
+// four waves share one (batch, kv-head): its list offsets, list entries and,
+// per indexed block, the score-table rows of its component codes are staged
+// in LDS once, so list walks and block scans never wait on global memory.
+// Codebook reads have wave-uniform addresses and go through scalar loads.
 //
 //  1. If E = qb - L + 1 <= R the selection is 0..E-1 (bypass).
 //  2. Rotate the query (fp32, products rounded before the add), score every
-//     code with an fp32 fused multiply-add chain in dimension order (the
-//     codebook of the kv-head is staged in LDS and read as broadcasts), keep
-//     the n_probes best codes of each component in registers.
+//     code with an fp32 fused multiply-add chain in dimension order, keep
+//     the n_probes best codes of each component.
 //  3. The n_probes best addresses: an address (x-th best of component 0,
 //     y-th best of component 1) has (x+1)(y+1)-1 addresses at least as good,
 //     so only pairs with (x+1)(y+1) <= n_probes can be among them.  tau is
-//     the key (sigma, address) of the n_probes-th best address.
-//  4. Walking an address in rank order adds the causally eligible prefix of
-//     its ascending list.  The walk stops once >= n_probes addresses were
-//     probed and >= R blocks collected; equivalently the pool is every
-//     indexed eligible block whose address key is <= max(tau, key_R), where
-//     key_R is the key of the R-th best indexed eligible block.  Lanes whose
-//     first n_probes addresses hold < R blocks need key_R: the wave scans
-//     the eligible blocks once (block codes are uniform, each lane reads its
-//     two component scores from LDS) keeping the R best block keys.
+//     the key of the n_probes-th best address.
+//  4. The walk in rank order stops once >= n_probes addresses were probed
+//     and >= R blocks collected; equivalently the pool is every indexed
+//     eligible block whose address key is <= max(tau, key_R), key_R being
+//     the key of the R-th best indexed eligible block.  Lanes whose first
+//     n_probes lists hold < R eligible blocks need key_R: the wave scans the
+//     eligible blocks once, keeping the R best block keys.
 //  5. Rerank: rho = fp32 fma chain <q_rot, kbar_n> in dimension order; the
 //     R best by (rho desc, block asc) are kept and written ascending.
+//
+// Ordered choices use 64-bit keys where a larger key is better: the high
+// word is the score mapped to an order-preserving unsigned integer, the low
+// word breaks ties toward the lower address / code / block.
 #include "common.hpp"
 
 namespace {
 
-struct Key {           // an address or block key: larger sig first, then lower a, then lower n
-    float sig;
-    int a;
-    int n;
-};
+typedef unsigned long long u64;
 
-__device__ __forceinline__ bool key_better(float s1, int a1, int n1, float s2, int a2, int n2) {
-    return s1 > s2 || (s1 == s2 && (a1 < a2 || (a1 == a2 && n1 < n2)));
+__device__ __forceinline__ uint32_t ordered(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// address/code/block keys: larger score first, then lower index
+__device__ __forceinline__ u64 key_of(float s, uint32_t low_rank) {
+    return ((u64)ordered(s) << 32) | (u64)low_rank;
+}
+
+// low word of a block key: lower address first, then lower block
+__device__ __forceinline__ uint32_t block_low(int a, int n) {
+    return (uint32_t)((4095 - a) << 13) | (uint32_t)(8191 - n);
+}
+
+template <int M>
+__device__ __forceinline__ void insert(u64 (&lst)[M], u64 k) {
+#pragma unroll
+    for (int x = 0; x < M; ++x) {
+        const u64 cur = lst[x];
+        const bool sw = k > cur;
+        lst[x] = sw ? k : cur;
+        k = sw ? cur : k;
+    }
 }
 
 template <int D, int P, int NPRM, int RM, bool BF16>
@@ -54,29 +77,56 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                                                const int32_t *__restrict__ addr,
                                                const int32_t *__restrict__ offsets,
                                                const int32_t *__restrict__ entries,
-                                               const int32_t *__restrict__ load,
                                                int32_t *__restrict__ sel) {
     constexpr int H = D / 2;
     constexpr int DS = D / P;
     extern __shared__ float lds[];
-    const int K = s.K, PK = P * K;
-    float *cb_s = lds;                               // [P*K][DS]
+    const int K = s.K, PK = P * K, A = s.A, NB = s.NB;
+    const int nw = blockDim.x / WAVE;
+    int2 *meta_s = reinterpret_cast<int2 *>(lds);                // [NB]: score rows, tie word
+    int *off_s = reinterpret_cast<int *>(meta_s + NB);           // [A+1]
+    int *ent_s = off_s + A + 1;                                  // [NB]
+    float *sc_all = reinterpret_cast<float *>(ent_s + NB);       // [nw][P*K][64]
     const int lane = lane_id(), wave = threadIdx.x / WAVE;
-    float *sc_s = lds + PK * DS + wave * PK * WAVE;  // [P*K][64] scores of this wave
+    float *sc_s = sc_all + wave * PK * WAVE;
 
     const int h = blockIdx.y, b = blockIdx.z, g = h / s.G;
-    for (int x = threadIdx.x; x < PK * DS / 4; x += blockDim.x)
-        reinterpret_cast<float4 *>(cb_s)[x] =
-            reinterpret_cast<const float4 *>(cb + (size_t)g * PK * DS)[x];
+    const size_t ug = (size_t)b * s.Hkv + g;
+    const int tw0 = blockIdx.x * nw * WAVE;                      // first token of the workgroup
+    const int R = s.R;
+    // blocks the workgroup can need: eligible for its last wave
+    const int nblk = min(NB, max(0, (min(s.T, tw0 + nw * WAVE) - 1) / s.beta - s.L + 1));
+    const bool any_search = nblk > R;
+    if (any_search) {
+        const int32_t *off_g = offsets + ug * (A + 1);
+        for (int x = threadIdx.x; x <= A; x += blockDim.x) off_s[x] = off_g[x];
+        const int32_t *ent_g = entries + ug * NB;
+        for (int x = threadIdx.x; x < NB; x += blockDim.x) ent_s[x] = ent_g[x];
+    }
+    __syncthreads();
+    if (any_search) {
+        const int32_t *ad_g = addr + ug * NB;
+        for (int n = threadIdx.x; n < nblk; n += blockDim.x) {
+            const int a = ad_g[n];
+            // kept blocks are the first `cap` of the address in source order,
+            // so n is indexed iff it is not after the list's last entry.
+            // x: byte offsets of the score-table rows of the block's two
+            // component codes (16 bits each), or -1 if it is not indexed;
+            // y: tie word (lower address first, then lower block)
+            const int c0 = P == 1 ? a : a / K, c1 = P == 1 ? 0 : a - c0 * K;
+            const bool idx = n <= ent_s[off_s[a + 1] - 1];
+            const int o0 = c0 * WAVE * 4, o1 = P == 1 ? 0 : (K + c1) * WAVE * 4;   // bytes
+            meta_s[n] = make_int2(idx ? o0 | (o1 << 16) : -1, (int)block_low(a, n));
+        }
+    }
     __syncthreads();
 
-    const int t0 = (blockIdx.x * (int)(blockDim.x / WAVE) + wave) * WAVE;
+    const int t0 = tw0 + wave * WAVE;
     if (t0 >= s.T) return;
     const int t = t0 + lane;
     const bool live = t < s.T;
     const int qb = t0 / s.beta;
     const int E = max(0, qb - s.L + 1);
-    const int R = s.R;
     int32_t *out = sel + (((size_t)b * s.Hq + h) * s.T + (live ? t : t0)) * R;
 
     if (E <= R) {  // bypass: every eligible block is selected
@@ -88,12 +138,12 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     // ---- rotated query (fp32, same rounding as the rotation's definition)
     float qr[D];
     {
-        const size_t base = (((size_t)b * s.T + t) * s.Hq + h) * D;
+        const size_t base = (((size_t)b * s.T + (live ? t : t0)) * s.Hq + h) * D;
         float x[D];
 #pragma unroll
         for (int j = 0; j < D; j += 8) load8<BF16>(q, base + j, x + j);
-        const float *cr = cos_t + (size_t)t * H;
-        const float *sr = sin_t + (size_t)t * H;
+        const float *cr = cos_t + (size_t)(live ? t : t0) * H;
+        const float *sr = sin_t + (size_t)(live ? t : t0) * H;
 #pragma unroll
         for (int i = 0; i < H; i += 4) {
             const float4 c4 = *reinterpret_cast<const float4 *>(cr + i);
@@ -110,53 +160,48 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
         }
     }
 
-    // ---- component scores; n_probes best codes per component
+    // ---- component scores; the n_probes best codes of each component
+    // (codes arrive in ascending order, so a strict compare keeps the lower
+    // code first on equal scores)
     float tv[P][NPRM];
     int tc[P][NPRM];
+    const float *cbg = cb + (size_t)g * PK * DS;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
 #pragma unroll
         for (int x = 0; x < NPRM; ++x) { tv[p][x] = -INFINITY; tc[p][x] = -1; }
+#pragma unroll 2
         for (int c = 0; c < K; ++c) {
-            const float *crow = cb_s + (p * K + c) * DS;
+            const float *crow = cbg + (p * K + c) * DS;
             float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < DS; j += 4) {
-                const float4 cv = *reinterpret_cast<const float4 *>(crow + j);
-                acc = __builtin_fmaf(qr[p * DS + j], cv.x, acc);
-                acc = __builtin_fmaf(qr[p * DS + j + 1], cv.y, acc);
-                acc = __builtin_fmaf(qr[p * DS + j + 2], cv.z, acc);
-                acc = __builtin_fmaf(qr[p * DS + j + 3], cv.w, acc);
-            }
+            for (int j = 0; j < DS; ++j) acc = __builtin_fmaf(qr[p * DS + j], crow[j], acc);
             sc_s[(p * K + c) * WAVE + lane] = acc;
-            // codes arrive in ascending order, so a strict compare keeps the
-            // lower code first on equal scores
             float v = acc;
             int cc = c;
 #pragma unroll
             for (int x = 0; x < NPRM; ++x) {
                 const bool sw = v > tv[p][x];
-                const float tvx = tv[p][x];
-                const int tcx = tc[p][x];
-                tv[p][x] = sw ? v : tvx;
-                tc[p][x] = sw ? cc : tcx;
-                v = sw ? tvx : v;
-                cc = sw ? tcx : cc;
+                const float ov = tv[p][x];
+                const int oc = tc[p][x];
+                tv[p][x] = sw ? v : ov;
+                tc[p][x] = sw ? cc : oc;
+                v = sw ? ov : v;
+                cc = sw ? oc : cc;
             }
         }
     }
 
-    // ---- the n_probes best addresses
-    const int A = s.A;
+    // ---- the n_probes best addresses (keys: sigma, then lower address)
     const int npr = min(s.npr, A);
-    float av[NPRM];
-    int aa[NPRM];
+    float bv[NPRM];
+    int ba[NPRM];
     if constexpr (P == 1) {
 #pragma unroll
-        for (int x = 0; x < NPRM; ++x) { av[x] = tv[0][x]; aa[x] = tc[0][x]; }
+        for (int x = 0; x < NPRM; ++x) { bv[x] = tv[0][x]; ba[x] = tc[0][x]; }
     } else {
 #pragma unroll
-        for (int x = 0; x < NPRM; ++x) { av[x] = -INFINITY; aa[x] = 0x7fffffff; }
+        for (int x = 0; x < NPRM; ++x) { bv[x] = -INFINITY; ba[x] = 0x7fffffff; }
 #pragma unroll
         for (int x = 0; x < NPRM; ++x) {
 #pragma unroll
@@ -167,38 +212,28 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                 int a = ok ? tc[0][x] * K + tc[1][y] : 0x7fffffff;
 #pragma unroll
                 for (int z = 0; z < NPRM; ++z) {
-                    const bool sw = v > av[z] || (v == av[z] && a < aa[z]);
-                    const float avz = av[z];
-                    const int aaz = aa[z];
-                    av[z] = sw ? v : avz;
-                    aa[z] = sw ? a : aaz;
-                    v = sw ? avz : v;
-                    a = sw ? aaz : a;
+                    const bool sw = (v > bv[z]) | ((v == bv[z]) & (a < ba[z]));
+                    const float ov = bv[z];
+                    const int oa = ba[z];
+                    bv[z] = sw ? v : ov;
+                    ba[z] = sw ? a : oa;
+                    v = sw ? ov : v;
+                    a = sw ? oa : a;
                 }
             }
         }
     }
-    float tau_s = av[0];
-    int tau_a = aa[0];
+    float tau_v = bv[0];
+    int tau_a = ba[0];
 #pragma unroll
     for (int x = 1; x < NPRM; ++x)
-        if (x == npr - 1) { tau_s = av[x]; tau_a = aa[x]; }
+        if (x == npr - 1) { tau_v = bv[x]; tau_a = ba[x]; }
 
     // ---- rerank state: RM slots, best first; the first RM-R are sentinels
-    float rv[RM];
-    int rn[RM];
+    u64 rk[RM];
 #pragma unroll
-    for (int x = 0; x < RM; ++x) {
-        const bool sent = x < RM - R;
-        rv[x] = sent ? INFINITY : -INFINITY;
-        rn[x] = sent ? -1 : 0x7fffffff;
-    }
-    const size_t ug = (size_t)b * s.Hkv + g;
-    const float *kb = kbar + ug * s.NB * D;
-    const int32_t *off = offsets + ug * (A + 1);
-    const int32_t *ent = entries + ug * s.NB;
-    const int32_t *ad = addr + ug * s.NB;
-    const int32_t *ldv = load + ug * A;
+    for (int x = 0; x < RM; ++x) rk[x] = x < RM - R ? ~0ull : 0ull;
+    const float *kb = kbar + ug * (size_t)NB * D;
     const int last = qb - s.L;
 
     auto rerank = [&](int n) {
@@ -212,18 +247,7 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
             acc = __builtin_fmaf(qr[j + 2], kv.z, acc);
             acc = __builtin_fmaf(qr[j + 3], kv.w, acc);
         }
-        float v = acc;
-        int nn = n;
-#pragma unroll
-        for (int x = 0; x < RM; ++x) {
-            const bool sw = v > rv[x] || (v == rv[x] && nn < rn[x]);
-            const float rvx = rv[x];
-            const int rnx = rn[x];
-            rv[x] = sw ? v : rvx;
-            rn[x] = sw ? nn : rnx;
-            v = sw ? rvx : v;
-            nn = sw ? rnx : nn;
-        }
+        insert(rk, key_of(acc, (uint32_t)(0x7FFFFFFF - n)));
     };
 
     // ---- pool part 1: the eligible prefixes of the n_probes best lists
@@ -231,14 +255,15 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     if (live) {
 #pragma unroll
         for (int x = 0; x < NPRM; ++x) {
-            if (x >= npr) break;
-            const int a = aa[x];
-            const int e1 = off[a + 1];
-            for (int e = off[a]; e < e1; ++e) {
-                const int n = ent[e];
-                if (n > last) break;
-                rerank(n);
-                ++cnt;
+            if (x < npr) {
+                const int a = ba[x];
+                const int e1 = off_s[a + 1];
+                for (int e = off_s[a]; e < e1; ++e) {
+                    const int n = ent_s[e];
+                    if (n > last) break;
+                    rerank(n);
+                    ++cnt;
+                }
             }
         }
     }
@@ -246,68 +271,61 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     // ---- pool part 2: extension to R blocks, for lanes that need it
     const bool need = live && cnt < R;
     if (__ballot(need) != 0ull) {
-        float kv_[RM];
-        int ka_[RM], kn_[RM];
+        u64 kk[RM];
 #pragma unroll
-        for (int x = 0; x < RM; ++x) {
-            const bool sent = x < RM - R;
-            kv_[x] = sent ? INFINITY : -INFINITY;
-            ka_[x] = sent ? -1 : 0x7fffffff;
-            kn_[x] = sent ? -1 : 0x7fffffff;
+        for (int x = 0; x < RM; ++x) kk[x] = x < RM - R ? ~0ull : 0ull;
+        const char *scl = reinterpret_cast<const char *>(sc_s + lane);
+        auto score = [&](int2 m) {
+            const int x = m.x < 0 ? 0 : m.x;
+            const float a0 = *reinterpret_cast<const float *>(scl + (x & 0xFFFF));
+            const float a1 = *reinterpret_cast<const float *>(scl + (x >> 16));
+            return P == 1 ? a0 : a0 + a1;
+        };
+        // a block enters the R best if its key beats the R-th best so far
+        auto visit = [&](float sg, int2 m) {
+            if (m.x < 0) return;  // not indexed (wave-uniform)
+            const u64 key = key_of(sg, (uint32_t)m.y);
+            if (need & (key > kk[RM - 1])) insert(kk, key);
+        };
+        constexpr int U = 8;
+        int n = 0;
+        for (; n + U <= last + 1; n += U) {
+            int2 m[U];
+            float sg[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) m[u] = meta_s[n + u];
+#pragma unroll
+            for (int u = 0; u < U; ++u) sg[u] = score(m[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) visit(sg[u], m[u]);
         }
-        const int cap = s.cap;
-        for (int n = 0; n <= last; ++n) {
-            const int a = uniform(ad[n]);
-            if (uniform(ldv[a]) > cap) {
-                // the list is full: n is kept iff it is not after its last entry
-                const int o = uniform(off[a]);
-                if (n > uniform(ent[o + cap - 1])) continue;
-            }
-            float sg;
-            if constexpr (P == 1) {
-                sg = sc_s[a * WAVE + lane];
-            } else {
-                const int c0 = a / K, c1 = a - c0 * K;
-                sg = sc_s[c0 * WAVE + lane] + sc_s[(K + c1) * WAVE + lane];
-            }
-            if (need) {
-                float v = sg;
-                int va = a, vn = n;
-#pragma unroll
-                for (int x = 0; x < RM; ++x) {
-                    const bool sw = key_better(v, va, vn, kv_[x], ka_[x], kn_[x]);
-                    const float kvx = kv_[x];
-                    const int kax = ka_[x], knx = kn_[x];
-                    kv_[x] = sw ? v : kvx;
-                    ka_[x] = sw ? va : kax;
-                    kn_[x] = sw ? vn : knx;
-                    v = sw ? kvx : v;
-                    va = sw ? kax : va;
-                    vn = sw ? knx : vn;
-                }
-            }
+        for (; n <= last; ++n) {
+            const int2 m = meta_s[n];
+            visit(score(m), m);
         }
         if (need) {
-            // blocks ranked after tau among the R best (the rest are in part 1)
+            // the R best blocks that rank after tau (the others are in part 1)
+            const uint32_t tau_hi = ordered(tau_v);
 #pragma unroll
             for (int x = 0; x < RM; ++x) {
-                if (x < RM - R) continue;
-                if (kn_[x] == 0x7fffffff) continue;   // fewer than R indexed eligible blocks
-                const bool after_tau =
-                    kv_[x] < tau_s || (kv_[x] == tau_s && ka_[x] > tau_a);
-                if (after_tau) rerank(kn_[x]);
+                if (x < RM - R || kk[x] == 0ull) continue;
+                const uint32_t hi = (uint32_t)(kk[x] >> 32);
+                const int a = 4095 - (int)((kk[x] >> 13) & 0xFFFu);
+                const int nn = 8191 - (int)(kk[x] & 0x1FFFu);
+                if (hi < tau_hi || (hi == tau_hi && a > tau_a)) rerank(nn);
             }
-            // the R-th block's address ties with it: its remaining eligible blocks
-            if (kn_[RM - 1] != 0x7fffffff) {
-                const int aR = ka_[RM - 1], nR = kn_[RM - 1];
-                const bool after_tau =
-                    kv_[RM - 1] < tau_s || (kv_[RM - 1] == tau_s && aR > tau_a);
-                if (after_tau) {
-                    const int e1 = off[aR + 1];
-                    for (int e = off[aR]; e < e1; ++e) {
-                        const int n = ent[e];
-                        if (n > last) break;
-                        if (n > nR) rerank(n);
+            // blocks of the R-th block's address after it tie with it
+            const u64 kR = kk[RM - 1];
+            if (kR != 0ull) {
+                const uint32_t hi = (uint32_t)(kR >> 32);
+                const int aR = 4095 - (int)((kR >> 13) & 0xFFFu);
+                const int nR = 8191 - (int)(kR & 0x1FFFu);
+                if (hi < tau_hi || (hi == tau_hi && aR > tau_a)) {
+                    const int e1 = off_s[aR + 1];
+                    for (int e = off_s[aR]; e < e1; ++e) {
+                        const int nn = ent_s[e];
+                        if (nn > last) break;
+                        if (nn > nR) rerank(nn);
                     }
                 }
             }
@@ -317,7 +335,9 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     // ---- emit the kept blocks ascending, -1 padded
     int o[RM];
 #pragma unroll
-    for (int x = 0; x < RM; ++x) o[x] = (x >= RM - R && rn[x] != 0x7fffffff) ? rn[x] : 0x7fffffff;
+    for (int x = 0; x < RM; ++x)
+        o[x] = (x >= RM - R && rk[x] != 0ull) ? 0x7FFFFFFF - (int)(rk[x] & 0xFFFFFFFFu)
+                                              : 0x7fffffff;
 #pragma unroll
     for (int pass = 0; pass < RM; ++pass) {
 #pragma unroll
@@ -344,14 +364,27 @@ __global__ __launch_bounds__(256) void k_route_bypass(Shape s, int32_t *__restri
     for (int r = 0; r < s.R; ++r) out[r] = r < E ? r : -1;
 }
 
+// LDS of one workgroup: per-block score rows and tie words, list offsets,
+// list entries and one score table per wave.
+size_t route_lds(const Shape &s, int waves) {
+    const int PK = s.P * s.K;
+    return (size_t)(s.A + 1 + 3 * s.NB) * sizeof(int) + (size_t)(waves * PK * WAVE) * sizeof(float);
+}
+
+// Four waves per workgroup unless that overflows the 160 KiB of LDS.
+int route_waves(const Shape &s) {
+    int w = 4;
+    while (w > 1 && route_lds(s, w) > 160 * 1024) w /= 2;
+    return w;
+}
+
 template <int D, int P, int NPRM, int RM, bool BF16>
 hipError_t launch_t(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
                     const float *cb, const float *kbar, const int32_t *addr,
-                    const int32_t *offsets, const int32_t *entries, const int32_t *load,
-                    int32_t *sel, hipStream_t st) {
-    const int PK = P * s.K;
-    const int waves = PK <= 64 ? 4 : 2;
-    const size_t lds = (size_t)(PK * (D / P) + waves * PK * WAVE) * sizeof(float);
+                    const int32_t *offsets, const int32_t *entries, int32_t *sel,
+                    hipStream_t st) {
+    const int waves = route_waves(s);
+    const size_t lds = route_lds(s, waves);
     const dim3 grid((unsigned)((s.T + waves * WAVE - 1) / (waves * WAVE)), (unsigned)s.Hq,
                     (unsigned)s.B);
     if (lds > 65536) {
@@ -361,26 +394,26 @@ hipError_t launch_t(const Shape &s, const void *q, const float *cos_t, const flo
         if (e != hipSuccess) return e;
     }
     k_route<D, P, NPRM, RM, BF16><<<grid, waves * WAVE, lds, st>>>(
-        s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, load, sel);
+        s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, sel);
     return hipGetLastError();
 }
 
 template <int D, int P, bool BF16>
 hipError_t launch_sel(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
                       const float *cb, const float *kbar, const int32_t *addr,
-                      const int32_t *offsets, const int32_t *entries, const int32_t *load,
-                      int32_t *sel, hipStream_t st) {
+                      const int32_t *offsets, const int32_t *entries, int32_t *sel,
+                      hipStream_t st) {
     if (s.npr <= 2 && s.R <= 2)
         return launch_t<D, P, 2, 2, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
-                                          load, sel, st);
+                                          sel, st);
     if (s.npr <= 4 && s.R <= 2)
         return launch_t<D, P, 4, 2, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
-                                          load, sel, st);
+                                          sel, st);
     if (s.npr <= 8 && s.R <= 8)
         return launch_t<D, P, 8, 8, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
-                                          load, sel, st);
+                                          sel, st);
     return launch_t<D, P, 16, 16, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
-                                        load, sel, st);
+                                        sel, st);
 }
 
 }  // namespace
@@ -389,13 +422,14 @@ hipError_t launch_route(const Shape &s, const void *q, const float *cos_t, const
                         const float *cb, const float *kbar, const int32_t *addr,
                         const int32_t *offsets, const int32_t *entries, const int32_t *load,
                         int32_t *sel, hipStream_t st) {
+    (void)load;
     if (s.NB - s.L <= s.R) {  // every query bypasses the search
         const long routes = (long)s.B * s.Hq * s.T;
         k_route_bypass<<<dim3((unsigned)((routes + 255) / 256)), 256, 0, st>>>(s, sel);
         return hipGetLastError();
     }
     const bool bf = s.dtype == 1;
-#define MONO_ROUTE_ARGS s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, load, sel, st
+#define MONO_ROUTE_ARGS s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, sel, st
     if (s.d == 64) {
         if (s.P == 1) return bf ? launch_sel<64, 1, true>(MONO_ROUTE_ARGS)
                                 : launch_sel<64, 1, false>(MONO_ROUTE_ARGS);
