@@ -8,12 +8,18 @@
 //
 // Every query carries its own remote blocks, so a tile of queries rarely
 // shares a remote block.  The work is regrouped by source block instead:
-//   plan     per 64-query tile: is every row's selection identical (always
-//            true under the bypass)?  If not, every (query, slot) with a
-//            valid, first-occurrence block takes a position in its
-//            (batch, kv-head, block) bin with an integer atomic.
+//   prep     per (batch, kv-head, 1024-token segment): for every 64-query tile
+//            of the group's q-heads, is every row's selection identical
+//            (always true under the bypass)?  If not, every (query, slot)
+//            with a valid, first-occurrence block takes a rank in its
+//            source-block bin from an LDS counter; the segment's per-bin
+//            counts go to global memory.  The same workgroup rotates the
+//            segment's q rows (all heads of the group) and k rows once and
+//            stores them in the activation dtype, so no later kernel reads
+//            the rotary table.
+//   binsum   per bin: exclusive prefix of the segments' counts.
 //   scan     bin starts and 256-row chunk starts (one workgroup).
-//   scatter  (query, slot) ids into bin order.
+//   scatter  (query, slot) ids into bin order (bin, then segment, then rank).
 //   remote   per chunk of one bin: the block's rotated K and transposed V in
 //            LDS, up to 256 gathered rotated query rows, S^T = K Q^T and
 //            O^T = V^T P^T on MFMA with an fp32 softmax; writes a normalized
@@ -22,8 +28,11 @@
 //            tiles, the shared remote blocks) with an online softmax and the
 //            causal mask, then the log-sum-exp merge of the tile's remote
 //            partials, in slot order.
-// The values a row gets never depend on which other rows share its tile, so
-// the result does not depend on the order the atomics hand out positions.
+// No global atomics are used.  The values a row gets never depend on which
+// other rows share its chunk, so results are deterministic.  Workgroup ids
+// are remapped so that consecutive work items (chunks of one bin, adjacent
+// query tiles of one head) land on the same XCD and share its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "mfma.hpp"
@@ -59,8 +68,8 @@ __device__ __forceinline__ void load4(const void *base, size_t i, float *o) {
 
 __device__ __forceinline__ void store4(u16 *p, const float *x) {
     uint2 w;
-    w.x = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+    w.x = pack_bf16x2(x[0], x[1]);
+    w.y = pack_bf16x2(x[2], x[3]);
     *reinterpret_cast<uint2 *>(p) = w;
 }
 
@@ -68,63 +77,116 @@ __device__ __forceinline__ void store4(float *p, const float *x) {
     *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
-// Stage 64 rotated rows into an LDS tile.  rowfn(r, off, t) gives the element
-// offset of row r and its position, or returns false for a zero row.
-template <int D, bool BF16, typename RowFn>
-__device__ __forceinline__ void stage_rotated(Elem<BF16> *dst, const void *src,
-                                              const float *__restrict__ cos_t,
-                                              const float *__restrict__ sin_t, RowFn rowfn) {
-    constexpr int H = D / 2, G4 = H / 4;
-    using T = Tile<D, BF16>;
-    for (int task = threadIdx.x; task < 64 * G4; task += blockDim.x) {
-        const int r = task / G4, i = (task % G4) * 4;
-        size_t off = 0;
-        int t = 0;
-        float o0[4] = {0.f, 0.f, 0.f, 0.f}, o1[4] = {0.f, 0.f, 0.f, 0.f};
-        if (rowfn(r, off, t)) {
-            float x0[4], x1[4];
-            load4<BF16>(src, off + i, x0);
-            load4<BF16>(src, off + i + H, x1);
-            const float4 c = *reinterpret_cast<const float4 *>(cos_t + (size_t)t * H + i);
-            const float4 sn = *reinterpret_cast<const float4 *>(sin_t + (size_t)t * H + i);
-            const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+
+
+// Workgroup id -> work item, so that consecutive items run on one XCD
+// (workgroups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    const int x = bid & 7, j = bid >> 3;
+    const int per = n >> 3, rem = n & 7;
+    return x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
+// Register-staged copies for software pipelining (256 threads): issue()
+// starts the global loads of a 64-row tile into registers, commit() writes
+// them to LDS later, so the loads of the next tile overlap the current
+// tile's compute.
+template <int D, bool BF16>
+struct RowStager {
+    using E = Elem<BF16>;
+    static constexpr int VE = 16 / sizeof(E);
+    static constexpr int PR = D / VE;             // 16-byte pieces per row
+    static constexpr int PER = 64 * PR / 256;     // pieces per thread
+    uint4 v[PER];
+    template <typename RowFn>
+    __device__ __forceinline__ void issue(const E *src, RowFn rowfn) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = x0[e] * cc[e], p1 = x1[e] * ss[e];
-                const float p2 = x1[e] * cc[e], p3 = x0[e] * ss[e];
-                o0[e] = p0 - p1;
-                o1[e] = p2 + p3;
+        for (int p = 0; p < PER; ++p) {
+            const int task = threadIdx.x + p * 256;
+            const int r = task / PR, c = (task % PR) * VE;
+            size_t off = 0;
+            v[p] = rowfn(r, off) ? *reinterpret_cast<const uint4 *>(src + off + c)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    __device__ __forceinline__ void commit(E *dst) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int task = threadIdx.x + p * 256;
+            const int r = task / PR, c = (task % PR) * VE;
+            *reinterpret_cast<uint4 *>(dst + r * Tile<D, BF16>::QS + c) = v[p];
+        }
+    }
+};
+
+template <int D, bool BF16>
+struct VtStager {
+    using E = Elem<BF16>;
+    static constexpr int VE = 16 / sizeof(E);
+    static constexpr int PER = 64 * (D / VE) / 256;
+    uint4 v[PER];
+    // rows row0 + kk * stride, kk < 64; consecutive threads take consecutive keys
+    __device__ __forceinline__ void issue(const E *src, size_t row0, size_t stride) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int task = threadIdx.x + p * 256;
+            const int kk = task & 63, d0 = (task >> 6) * VE;
+            v[p] = *reinterpret_cast<const uint4 *>(src + row0 + (size_t)kk * stride + d0);
+        }
+    }
+    __device__ __forceinline__ void commit(E *dst) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int task = threadIdx.x + p * 256;
+            const int kk = task & 63, d0 = (task >> 6) * VE;
+            const E *x = reinterpret_cast<const E *>(&v[p]);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) dst[(d0 + e) * Tile<D, BF16>::VS + kk] = x[e];
+        }
+    }
+};
+
+// The wave's Q^T fragments for one query row per lane (row offset `off`
+// elements, all-zero if !ok): dims 32c + 8(l/16) .. +7 for c < D/32.
+template <int D, bool BF16>
+struct QFrags {
+    using E = Elem<BF16>;
+    static constexpr int VE = 16 / sizeof(E);
+    static constexpr int NV = 8 / VE;   // 16-byte loads per 8 elements
+    uint4 raw[D / 32][NV];
+    __device__ __forceinline__ void issue(const E *src, size_t off, bool ok) {
+        const int lg = lane_id() >> 4;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+            for (int u = 0; u < NV; ++u)
+                raw[c][u] = ok ? *reinterpret_cast<const uint4 *>(src + off + 32 * c + 8 * lg + u * VE)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __device__ __forceinline__ void get(Frag8<BF16> (&f)[D / 32]) const {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+            if constexpr (BF16) {
+                f[c].v = __builtin_bit_cast(bf16x8, raw[c][0]);
+            } else {
+                const float *x0 = reinterpret_cast<const float *>(&raw[c][0]);
+                const float *x1 = reinterpret_cast<const float *>(&raw[c][NV - 1]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[c].v[e] = x0[e];
+                    f[c].v[4 + e] = x1[e];
+                }
             }
         }
-        store4(dst + r * T::QS + i, o0);
-        store4(dst + r * T::QS + i + H, o1);
     }
-}
+};
 
-// Stage V rows [row0, row0 + 64) (row stride `stride` elements) transposed:
-// dst[d][key].  Rows at or past `nvalid` are zero.
+// One wave, 16 queries (B fragments of Q^T in registers: lane l holds row
+// l%16, dims 32c + 8(l/16) .. +7) against 64 keys, folded into the running
+// softmax state (m, l in log2 units, o unnormalized).  Keys with global index
+// > qlimit are masked (causality).
 template <int D, bool BF16>
-__device__ __forceinline__ void stage_vt(Elem<BF16> *dst, const void *v, size_t row0, size_t stride,
-                                         int nvalid) {
-    using T = Tile<D, BF16>;
-    constexpr int DG = D / 4;
-    for (int task = threadIdx.x; task < 64 * DG; task += blockDim.x) {
-        const int kk = task / DG, d0 = (task % DG) * 4;
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (kk < nvalid) load4<BF16>(v, row0 + (size_t)kk * stride + d0, x);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if constexpr (BF16) dst[(d0 + e) * T::VS + kk] = f32_to_bf16_bits(x[e]);
-            else dst[(d0 + e) * T::VS + kk] = x[e];
-        }
-    }
-}
-
-// One wave, 16 queries (its rows of the Q tile) against 64 keys, folded into
-// the running softmax state (m, l in log2 units, o unnormalized).  Keys with
-// global index > qlimit are masked (causality).
-template <int D, bool BF16>
-__device__ __forceinline__ void attend64(const Elem<BF16> *Qw, const Elem<BF16> *Ks,
+__device__ __forceinline__ void attend64(const Frag8<BF16> (&qf)[D / 32], const Elem<BF16> *Ks,
                                          const Elem<BF16> *Vt, float sl2, int key0, int qlimit,
                                          f32x4 (&o)[D / 16], float &m, float &l) {
     using T = Tile<D, BF16>;
@@ -134,11 +196,10 @@ __device__ __forceinline__ void attend64(const Elem<BF16> *Qw, const Elem<BF16> 
     for (int mt = 0; mt < 4; ++mt) st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-        const Frag8<BF16> qf = lds_frag8(Qw + lr * T::QS + 32 * c + 8 * lg);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const Frag8<BF16> kf = lds_frag8(Ks + (mt * 16 + lr) * T::QS + 32 * c + 8 * lg);
-            mma32(st[mt], kf, qf);
+            mma32(st[mt], kf, qf[c]);
         }
     }
     float mx = m;
@@ -155,7 +216,7 @@ __device__ __forceinline__ void attend64(const Elem<BF16> *Qw, const Elem<BF16> 
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const bool none = mx == -INFINITY;
-    const float alpha = none ? 1.0f : exp2f(m - mx);
+    const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m - mx);
     float p[4][4];
     float ps = 0.0f;
 #pragma unroll
@@ -163,7 +224,7 @@ __device__ __forceinline__ void attend64(const Elem<BF16> *Qw, const Elem<BF16> 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float z = st[mt][r];
-            p[mt][r] = (z == -INFINITY) ? 0.0f : exp2f(z - mx);
+            p[mt][r] = (z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - mx);
             ps += p[mt][r];
         }
     }
@@ -187,64 +248,161 @@ __device__ __forceinline__ void attend64(const Elem<BF16> *Qw, const Elem<BF16> 
     }
 }
 
-__global__ void k_fill_i32(int32_t *p, long n, int32_t v) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
-}
 
-// One wave per 64-query tile.
-__global__ __launch_bounds__(256) void k_attn_plan(Shape s, const int32_t *__restrict__ sel,
-                                                   int32_t *__restrict__ count,
-                                                   int32_t *__restrict__ entry_pos,
-                                                   int32_t *__restrict__ tile_flag) {
-    const int lane = lane_id(), wave = threadIdx.x / WAVE;
-    const long ntiles = (long)s.B * s.Hq * (s.T / 64);
-    const long tile = (long)blockIdx.x * 4 + wave;
-    if (tile >= ntiles) return;
-    const int tt = (int)(tile % (s.T / 64));
-    const long bh = tile / (s.T / 64);
-    const int h = (int)(bh % s.Hq), b = (int)(bh / s.Hq), g = h / s.G;
-    const int t0 = tt * 64, qb = t0 / s.beta, last = qb - s.L, R = s.R;
-    const long route0 = bh * s.T + t0;
-    const long route = route0 + lane;
-    const int32_t *row = sel + route * R;
-    const int32_t *row0 = sel + route0 * R;
-    bool same = true;
-    for (int r = 0; r < R; ++r) same = same && row[r] == row0[r];
-    const bool uni = __ballot(!same) == 0ull;
-    if (lane == 0) tile_flag[tile] = uni ? 1 : 0;
-    int32_t *ep = entry_pos + route * R;
-    for (int r = 0; r < R; ++r) {
-        const int id = row[r];
-        bool valid = !uni && id >= 0 && id <= last;
-        for (int r2 = 0; valid && r2 < r; ++r2) valid = row[r2] != id;
-        int pos = -1;
-        if (valid) pos = atomicAdd(&count[((size_t)b * s.Hkv + g) * s.NB + id], 1);
-        ep[r] = pos;
-    }
-}
-
+constexpr int SEG = 1024;          // tokens per prep segment
 constexpr int SCAN_THREADS = 1024;
 constexpr int CHUNK_ROWS = 256;
 
-__global__ __launch_bounds__(SCAN_THREADS) void k_attn_scan(int nbins, const int32_t *__restrict__ count,
-                                                            int32_t *__restrict__ bin_start,
-                                                            int32_t *__restrict__ chunk_start,
-                                                            int32_t *__restrict__ total_chunks) {
-    __shared__ int32_t ps[SCAN_THREADS], pc[SCAN_THREADS];
+__global__ __launch_bounds__(256) void k_attn_prep(Shape s, const int32_t *__restrict__ sel,
+                                                   int32_t *__restrict__ cnt,
+                                                   int32_t *__restrict__ entry_pos,
+                                                   int32_t *__restrict__ tile_flag, int nseg) {
+    extern __shared__ int hist[];   // [NB]
+    const int seg = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int T_ = s.T, Hq = s.Hq, Hkv = s.Hkv, G = s.G, R = s.R, NB = s.NB;
+    const int t_beg = seg * SEG, t_end = min(T_, t_beg + SEG);
+    const int lane = lane_id(), wave = threadIdx.x / WAVE, nw = blockDim.x / WAVE;
+    for (int n = threadIdx.x; n < NB; n += blockDim.x) hist[n] = 0;
+    __syncthreads();
+
+    const int ntile = (t_end - t_beg) / 64;
+    for (int task = wave; task < G * ntile; task += nw) {
+        const int hl = task / ntile, tl = task % ntile;
+        const int h = g * G + hl, t0 = t_beg + tl * 64;
+        const int qb = t0 / s.beta, last = qb - s.L;
+        const long route0 = ((long)b * Hq + h) * T_ + t0;
+        const long route = route0 + lane;
+        const int32_t *row = sel + route * R;
+        const int32_t *row0 = sel + route0 * R;
+        bool same = true;
+        for (int r = 0; r < R; ++r) same = same && row[r] == row0[r];
+        const bool uni = __ballot(!same) == 0ull;
+        if (lane == 0) tile_flag[((long)b * Hq + h) * (T_ / 64) + t0 / 64] = uni ? 1 : 0;
+        int32_t *ep = entry_pos + route * R;
+        for (int r = 0; r < R; ++r) {
+            const int id = row[r];
+            bool valid = !uni && id >= 0 && id <= last;
+            for (int r2 = 0; valid && r2 < r; ++r2) valid = row[r2] != id;
+            ep[r] = valid ? atomicAdd(&hist[id], 1) : -1;
+        }
+    }
+    __syncthreads();
+    int32_t *cg = cnt + ((size_t)b * Hkv + g) * NB * nseg;
+    for (int n = threadIdx.x; n < NB; n += blockDim.x) cg[(size_t)n * nseg + seg] = hist[n];
+
+}
+
+// Rotate every q and k row once into the activation dtype (grid-wide stream;
+// one thread per 4 rotation pairs; rows of one position are adjacent so the
+// rotary table row is read once from cache for all heads).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_attn_rotate(Shape s, const void *__restrict__ q,
+                                                     const void *__restrict__ k,
+                                                     const float *__restrict__ cos_t,
+                                                     const float *__restrict__ sin_t,
+                                                     Elem<BF16> *__restrict__ q_rot,
+                                                     Elem<BF16> *__restrict__ k_rot) {
+    constexpr int H = D / 2, PT = H / 4;
+    const int heads = s.Hq + s.Hkv;
+    const long total = (long)s.B * s.T * heads * PT;
+    for (long task = (long)blockIdx.x * blockDim.x + threadIdx.x; task < total;
+         task += (long)gridDim.x * blockDim.x) {
+        const int i = (int)(task % PT) * 4;
+        const long row = task / PT;               // (b, t, head) with head fastest
+        const int hd = (int)(row % heads);
+        const long bt = row / heads;
+        const int t = (int)(bt % s.T);
+        size_t off;
+        const void *src;
+        Elem<BF16> *dst;
+        if (hd < s.Hq) {
+            off = ((size_t)bt * s.Hq + hd) * D;
+            src = q;
+            dst = q_rot;
+        } else {
+            off = ((size_t)bt * s.Hkv + (hd - s.Hq)) * D;
+            src = k;
+            dst = k_rot;
+        }
+        float x0[4], x1[4], o0[4], o1[4];
+        load4<BF16>(src, off + i, x0);
+        load4<BF16>(src, off + i + H, x1);
+        const float4 c = *reinterpret_cast<const float4 *>(cos_t + (size_t)t * H + i);
+        const float4 sn = *reinterpret_cast<const float4 *>(sin_t + (size_t)t * H + i);
+        const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = x0[e] * cc[e], p1 = x1[e] * ss[e];
+            const float p2 = x1[e] * cc[e], p3 = x0[e] * ss[e];
+            o0[e] = p0 - p1;
+            o1[e] = p2 + p3;
+        }
+        store4(dst + off + i, o0);
+        store4(dst + off + i + H, o1);
+    }
+}
+
+constexpr int BIN_WG = 256;
+
+// Per bin: exclusive prefix over segments; per workgroup of 256 bins: the
+// exclusive scan of bin sizes and of 256-row chunk counts, and their totals.
+__global__ __launch_bounds__(BIN_WG) void k_attn_binsum(int nbins, int nseg,
+                                                        const int32_t *__restrict__ cnt,
+                                                        int32_t *__restrict__ seg_rel,
+                                                        int32_t *__restrict__ bin_local,
+                                                        int32_t *__restrict__ chunk_local,
+                                                        int32_t *__restrict__ wg_sum) {
+    __shared__ int32_t ps[BIN_WG], pc[BIN_WG];
     const int tid = threadIdx.x;
-    const int per = (nbins + SCAN_THREADS - 1) / SCAN_THREADS;
-    const int lo = min(nbins, tid * per), hi = min(nbins, lo + per);
+    const long bin = (long)blockIdx.x * BIN_WG + tid;
+    int acc = 0;
+    if (bin < nbins) {
+        const int32_t *c = cnt + bin * nseg;
+        int32_t *o = seg_rel + bin * nseg;
+        for (int sg = 0; sg < nseg; ++sg) {
+            const int x = c[sg];
+            o[sg] = acc;
+            acc += x;
+        }
+    }
+    const int nch = (acc + CHUNK_ROWS - 1) / CHUNK_ROWS;
+    ps[tid] = acc;
+    pc[tid] = nch;
+    __syncthreads();
+    for (int off = 1; off < BIN_WG; off <<= 1) {  // inclusive Hillis-Steele scan
+        const int a = tid >= off ? ps[tid - off] : 0;
+        const int c = tid >= off ? pc[tid - off] : 0;
+        __syncthreads();
+        ps[tid] += a;
+        pc[tid] += c;
+        __syncthreads();
+    }
+    if (bin < nbins) {
+        bin_local[bin] = ps[tid] - acc;
+        chunk_local[bin] = pc[tid] - nch;
+    }
+    if (tid == BIN_WG - 1) {
+        wg_sum[2 * blockIdx.x] = ps[tid];
+        wg_sum[2 * blockIdx.x + 1] = pc[tid];
+    }
+}
+
+// Exclusive scan of the workgroup totals (one workgroup); the grand totals
+// go after the last workgroup.
+__global__ __launch_bounds__(1024) void k_attn_scan(int nwg, int32_t *__restrict__ wg_sum) {
+    __shared__ int32_t ps[1024], pc[1024];
+    const int tid = threadIdx.x;
+    const int per = (nwg + 1023) / 1024;
+    const int lo = min(nwg, tid * per), hi = min(nwg, lo + per);
     int s0 = 0, c0 = 0;
     for (int i = lo; i < hi; ++i) {
-        const int c = count[i];
-        s0 += c;
-        c0 += (c + CHUNK_ROWS - 1) / CHUNK_ROWS;
+        s0 += wg_sum[2 * i];
+        c0 += wg_sum[2 * i + 1];
     }
     ps[tid] = s0;
     pc[tid] = c0;
     __syncthreads();
-    for (int off = 1; off < SCAN_THREADS; off <<= 1) {  // inclusive Hillis-Steele scan
+    for (int off = 1; off < 1024; off <<= 1) {
         const int a = tid >= off ? ps[tid - off] : 0;
         const int c = tid >= off ? pc[tid - off] : 0;
         __syncthreads();
@@ -254,45 +412,68 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_attn_scan(int nbins, const int
     }
     int rs = tid ? ps[tid - 1] : 0, rc = tid ? pc[tid - 1] : 0;
     for (int i = lo; i < hi; ++i) {
-        bin_start[i] = rs;
-        chunk_start[i] = rc;
-        const int c = count[i];
-        rs += c;
-        rc += (c + CHUNK_ROWS - 1) / CHUNK_ROWS;
+        const int a = wg_sum[2 * i], c = wg_sum[2 * i + 1];
+        wg_sum[2 * i] = rs;
+        wg_sum[2 * i + 1] = rc;
+        rs += a;
+        rc += c;
     }
-    if (tid == SCAN_THREADS - 1) {
-        bin_start[nbins] = ps[tid];
-        chunk_start[nbins] = pc[tid];
-        total_chunks[0] = pc[tid];
+    if (tid == 1023) {
+        wg_sum[2 * nwg] = ps[tid];
+        wg_sum[2 * nwg + 1] = pc[tid];
     }
 }
 
-__global__ __launch_bounds__(256) void k_attn_scatter(Shape s, const int32_t *__restrict__ sel,
-                                                      const int32_t *__restrict__ entry_pos,
-                                                      const int32_t *__restrict__ bin_start,
-                                                      int32_t *__restrict__ list) {
+__device__ __forceinline__ int bin_start_of(const int32_t *bin_local, const int32_t *wg_base,
+                                            long bin) {
+    return wg_base[2 * (bin / BIN_WG)] + bin_local[bin];
+}
+
+// Scatter (query, slot) ids into bin order and replace each entry's rank by
+// its list position (where its partial state will be written); threads
+// below nbins also write their bin's entries of the chunk table.
+__global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbins,
+                                                      const int32_t *__restrict__ sel,
+                                                      int32_t *__restrict__ entry_pos,
+                                                      const int32_t *__restrict__ bin_local,
+                                                      const int32_t *__restrict__ chunk_local,
+                                                      const int32_t *__restrict__ wg_base,
+                                                      const int32_t *__restrict__ seg_rel,
+                                                      int32_t *__restrict__ list,
+                                                      int32_t *__restrict__ list_q,
+                                                      int32_t *__restrict__ chunk_bin) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nbins) {
+        const long nb = (long)nbins;
+        const int c0 = wg_base[2 * (i / BIN_WG) + 1] + chunk_local[i];
+        const int c1 = i + 1 < nb ? wg_base[2 * ((i + 1) / BIN_WG) + 1] + chunk_local[i + 1]
+                                  : wg_base[2 * ((nb + BIN_WG - 1) / BIN_WG) + 1];
+        for (int c = c0; c < c1; ++c) chunk_bin[c] = (int32_t)i;
+    }
     const long n = (long)s.B * s.Hq * s.T * s.R;
     if (i >= n) return;
     const int pos = entry_pos[i];
     if (pos < 0) return;
     const long route = i / s.R;
+    const int t = (int)(route % s.T);
     const int h = (int)((route / s.T) % s.Hq), b = (int)(route / ((long)s.T * s.Hq));
-    const int g = h / s.G;
-    const int id = sel[i];
-    list[bin_start[((size_t)b * s.Hkv + g) * s.NB + id] + pos] = (int32_t)i;
+    const long bin = ((long)b * s.Hkv + h / s.G) * s.NB + sel[i];
+    const int at = bin_start_of(bin_local, wg_base, bin) + seg_rel[bin * nseg + t / SEG] + pos;
+    list_q[at] = (int32_t)(((long)b * s.T + t) * s.Hq + h);   // row of q_rot
+    entry_pos[i] = at;                                         // where its partial will be
 }
 
 template <int D, int BETA, bool BF16>
-__global__ __launch_bounds__(256) void k_attn_remote(Shape s, const void *__restrict__ q,
-                                                     const void *__restrict__ k,
-                                                     const void *__restrict__ v,
-                                                     const float *__restrict__ cos_t,
-                                                     const float *__restrict__ sin_t,
+__global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
+                                                     const Elem<BF16> *__restrict__ k_rot,
+                                                     const Elem<BF16> *__restrict__ v,
                                                      const int32_t *__restrict__ list,
-                                                     const int32_t *__restrict__ bin_start,
-                                                     const int32_t *__restrict__ chunk_start,
-                                                     const int32_t *__restrict__ total_chunks,
+                                                     const int32_t *__restrict__ list_q,
+                                                     const int32_t *__restrict__ bin_local,
+                                                     const int32_t *__restrict__ chunk_local,
+                                                     const int32_t *__restrict__ wg_base,
+                                                     const int32_t *__restrict__ chunk_bin,
+                                                     int nbins,
                                                      float *__restrict__ part_lse,
                                                      Elem<BF16> *__restrict__ part_o) {
     using T = Tile<D, BF16>;
@@ -301,95 +482,115 @@ __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const void *__rest
     extern __shared__ __align__(16) unsigned char smem[];
     E *Ks = reinterpret_cast<E *>(smem);               // NSUB x [64][QS]
     E *Vts = Ks + NSUB * T::K_ELEMS;                    // NSUB x [D][VS]
-    E *Qs = Vts + NSUB * T::V_ELEMS;                    // [64][QS]
 
-    const int chunk = blockIdx.x;
-    if (chunk >= total_chunks[0]) return;
-    const int nbins = s.B * s.Hkv * s.NB;
-    int lo = 0, hi = nbins;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (chunk_start[mid] <= chunk) lo = mid;
-        else hi = mid;
-    }
-    const int bin = lo;
-    const int r0 = bin_start[bin] + (chunk - chunk_start[bin]) * CHUNK_ROWS;
-    const int r1 = min(r0 + CHUNK_ROWS, bin_start[bin + 1]);
-    const int n = bin % s.NB, g = (bin / s.NB) % s.Hkv, b = bin / (s.NB * s.Hkv);
-    const int T_ = s.T, Hkv = s.Hkv, Hq = s.Hq, R = s.R;
-
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-        const int tb = n * BETA + sub * 64;
-        stage_rotated<D, BF16>(Ks + sub * T::K_ELEMS, k, cos_t, sin_t,
-                               [&](int r, size_t &off, int &t) {
-                                   t = tb + r;
-                                   off = (((size_t)b * T_ + t) * Hkv + g) * D;
-                                   return true;
-                               });
-        stage_vt<D, BF16>(Vts + sub * T::V_ELEMS, v, (((size_t)b * T_ + tb) * Hkv + g) * D,
-                          (size_t)Hkv * D, 64);
-    }
-    const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+    const int nwg = (nbins + BIN_WG - 1) / BIN_WG;
+    const int nchunks = wg_base[2 * nwg + 1];
+    const int per = (nchunks + gridDim.x - 1) / gridDim.x;
+    const int c_beg = blockIdx.x * per, c_end = min(nchunks, c_beg + per);
+    const int T_ = s.T, Hkv = s.Hkv;
     const int lane = lane_id(), wave = threadIdx.x / WAVE, lr = lane & 15, lg = lane >> 4;
-    for (int rb = r0; rb < r1; rb += 64) {
-        __syncthreads();
-        stage_rotated<D, BF16>(Qs, q, cos_t, sin_t, [&](int r, size_t &off, int &t) {
-            const int row = rb + r;
-            if (row >= r1) return false;
-            const long route = list[row] / R;
-            t = (int)(route % T_);
-            const int hq = (int)((route / T_) % Hq);
-            off = (((size_t)b * T_ + t) * Hq + hq) * D;
-            return true;
-        });
-        __syncthreads();
-        f32x4 o[D / 16];
+    const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+    int loaded_bin = -1;
+    for (int chunk = c_beg; chunk < c_end; ++chunk) {
+        const int bin = chunk_bin[chunk];
+        const int bstart = bin_start_of(bin_local, wg_base, bin);
+        const int bend = bin + 1 < nbins ? bin_start_of(bin_local, wg_base, bin + 1) : wg_base[2 * nwg];
+        const int cstart = wg_base[2 * (bin / BIN_WG) + 1] + chunk_local[bin];
+        const int r0 = bstart + (chunk - cstart) * CHUNK_ROWS;
+        const int r1 = min(r0 + CHUNK_ROWS, bend);
+        const int n = bin % s.NB, g = (bin / s.NB) % s.Hkv, b = bin / (s.NB * s.Hkv);
+
+        // a row's entry id and q row, or -1 past the chunk
+        auto entry_of = [&](int grp) {
+            const int row = r0 + grp * 16 + lr;
+            return row < r1 ? make_int2(row, list_q[row]) : make_int2(-1, 0);
+        };
+        const int ngrp = (r1 - r0 + 15) / 16;
+        int grp = wave;
+        int2 e_cur = grp < ngrp ? entry_of(grp) : make_int2(-1, 0);
+        QFrags<D, BF16> qcur;
+        qcur.issue(q_rot, (size_t)e_cur.y * D, e_cur.x >= 0);
+
+        if (bin != loaded_bin) {   // consecutive chunks of one bin keep K/V in LDS
+            RowStager<D, BF16> ks[NSUB];
+            VtStager<D, BF16> vs[NSUB];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m = -INFINITY, l = 0.0f;
+            for (int sub = 0; sub < NSUB; ++sub) {
+                const int tb = n * BETA + sub * 64;
+                ks[sub].issue(k_rot, [&](int r, size_t &off) {
+                    off = (((size_t)b * T_ + tb + r) * Hkv + g) * D;
+                    return true;
+                });
+                vs[sub].issue(v, (((size_t)b * T_ + tb) * Hkv + g) * D, (size_t)Hkv * D);
+            }
+            __syncthreads();   // the previous chunk is done with Ks / Vts
 #pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub)
-            attend64<D, BF16>(Qs + wave * 16 * T::QS, Ks + sub * T::K_ELEMS, Vts + sub * T::V_ELEMS,
-                              sl2, 0, 0x7fffffff, o, m, l);
-        const int row = rb + wave * 16 + lr;
-        if (row < r1) {
-            const int e = list[row];
-            if (lg == 0) part_lse[e] = m + log2f(l);
-            const float inv = 1.0f / l;
+            for (int sub = 0; sub < NSUB; ++sub) {
+                ks[sub].commit(Ks + sub * T::K_ELEMS);
+                vs[sub].commit(Vts + sub * T::V_ELEMS);
+            }
+            __syncthreads();
+            loaded_bin = bin;
+        }
+
+        int2 e_next = grp + 4 < ngrp ? entry_of(grp + 4) : make_int2(-1, 0);
+        for (; grp < ngrp; grp += 4) {
+            Frag8<BF16> qf[D / 32];
+            qcur.get(qf);
+            // next group's Q in flight during this group's compute
+            const int e_now = e_cur.x;
+            if (grp + 4 < ngrp) qcur.issue(q_rot, (size_t)e_next.y * D, e_next.x >= 0);
+            e_cur = e_next;
+            e_next = grp + 8 < ngrp ? entry_of(grp + 8) : make_int2(-1, 0);
+            f32x4 o[D / 16];
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                const float x[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
-                store4(part_o + (size_t)e * D + dt * 16 + 4 * lg, x);
+            for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float m = -INFINITY, l = 0.0f;
+#pragma unroll
+            for (int sub = 0; sub < NSUB; ++sub)
+                attend64<D, BF16>(qf, Ks + sub * T::K_ELEMS, Vts + sub * T::V_ELEMS, sl2, 0,
+                                  0x7fffffff, o, m, l);
+            if (e_now >= 0) {
+                if (lg == 0) part_lse[e_now] = m + __builtin_amdgcn_logf(l);
+                const float inv = 1.0f / l;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) {
+                    const float x[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv,
+                                        o[dt][3] * inv};
+                    store4(part_o + (size_t)e_now * D + dt * 16 + 4 * lg, x);
+                }
             }
         }
     }
 }
 
 template <int D, int BETA, bool BF16>
-__global__ __launch_bounds__(256) void k_attn_local(Shape s, const void *__restrict__ q,
-                                                    const void *__restrict__ k,
-                                                    const void *__restrict__ v,
-                                                    const float *__restrict__ cos_t,
-                                                    const float *__restrict__ sin_t,
+__global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
+                                                    const Elem<BF16> *__restrict__ k_rot,
+                                                    const Elem<BF16> *__restrict__ v,
                                                     const int32_t *__restrict__ sel,
                                                     const int32_t *__restrict__ tile_flag,
                                                     const int32_t *__restrict__ entry_pos,
                                                     const float *__restrict__ part_lse,
                                                     const Elem<BF16> *__restrict__ part_o,
-                                                    void *__restrict__ out) {
+                                                    Elem<BF16> *__restrict__ out) {
     using T = Tile<D, BF16>;
     using E = Elem<BF16>;
     extern __shared__ __align__(16) unsigned char smem[];
-    E *Qs = reinterpret_cast<E *>(smem);
-    E *Ks = Qs + T::Q_ELEMS;
+    E *Ks = reinterpret_cast<E *>(smem);
     E *Vt = Ks + T::K_ELEMS;
     int *blk_s = reinterpret_cast<int *>(Vt + T::V_ELEMS);  // [R] shared remote blocks
 
-    const int ntt = s.T / 64, nbh = s.B * s.Hq;
-    // latest tiles first: they have the most blocks
-    const int tt = ntt - 1 - (int)(blockIdx.x / nbh);
-    const int bh = (int)(blockIdx.x % nbh);
+    const int ntt = s.T / 64;
+    // each workgroup walks a contiguous run of items: the tiles of one
+    // (batch, head), latest first, so adjacent tiles share K/V in its L2
+    const int nitems = s.B * s.Hq * ntt;
+    const int per = (nitems + gridDim.x - 1) / gridDim.x;
+    const int i_end = min(nitems, (int)blockIdx.x * per + per);
+    for (int item = blockIdx.x * per; item < i_end; ++item) {
+    __syncthreads();   // the previous item is done with LDS
+    const int tt = ntt - 1 - item % ntt;
+    const int bh = item / ntt;
     const int h = bh % s.Hq, b = bh / s.Hq, g = h / s.G;
     const int t0 = tt * 64, qb = t0 / BETA, R = s.R, L = s.L;
     const int T_ = s.T, Hkv = s.Hkv, Hq = s.Hq;
@@ -397,11 +598,19 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const void *__restr
     const bool uni = tile_flag[tile] != 0;
     const long route0 = (long)bh * T_ + t0;
 
-    stage_rotated<D, BF16>(Qs, q, cos_t, sin_t, [&](int r, size_t &off, int &t) {
-        t = t0 + r;
-        off = (((size_t)b * T_ + t) * Hq + h) * D;
-        return true;
-    });
+    const int lane = lane_id(), wave = threadIdx.x / WAVE, lr = lane & 15, lg = lane >> 4;
+    const int tq = t0 + wave * 16 + lr;  // this lane's query position
+    QFrags<D, BF16> qst;
+    qst.issue(q_rot, (((size_t)b * T_ + tq) * Hq + h) * D, true);
+    // merge inputs of this lane's query, in flight from the start
+    const long route = route0 + wave * 16 + lr;
+    constexpr int RP = 4;   // slots whose partial state is prefetched
+    int ep_pre[RP];
+    float lse_pre[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) ep_pre[r] = (!uni && r < R) ? entry_pos[route * R + r] : -1;
+#pragma unroll
+    for (int r = 0; r < RP; ++r) lse_pre[r] = ep_pre[r] >= 0 ? part_lse[ep_pre[r]] : 0.0f;
     if (uni) {  // shared remote blocks of the tile: valid first occurrences of row 0
         const int32_t *row0 = sel + route0 * R;
         for (int r = threadIdx.x; r < R; r += blockDim.x) {
@@ -413,39 +622,68 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const void *__restr
     }
     __syncthreads();
 
-    const int lane = lane_id(), wave = threadIdx.x / WAVE, lr = lane & 15, lg = lane >> 4;
-    const int tq = t0 + wave * 16 + lr;  // this lane's query position
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
     f32x4 o[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.0f;
 
+    // work items: (block, 64-key sub-tile) in order, skipping sub-tiles after the tile
     const int nrem = uni ? R : 0;
     const int lo_blk = max(0, qb - L + 1);
     const int nblk = nrem + (qb - lo_blk + 1);
-    for (int j = 0; j < nblk; ++j) {
+    auto item_key0 = [&](int j, int sub) {   // first key of item, or -1 if absent
         const int blk = j < nrem ? blk_s[j] : lo_blk + (j - nrem);
-        if (blk < 0) continue;
-        for (int sub = 0; sub < BETA / 64; ++sub) {
-            const int kb0 = blk * BETA + sub * 64;
-            if (kb0 > t0 + 63) break;  // entirely after every query of the tile
-            __syncthreads();
-            stage_rotated<D, BF16>(Ks, k, cos_t, sin_t, [&](int r, size_t &off, int &t) {
-                t = kb0 + r;
-                off = (((size_t)b * T_ + t) * Hkv + g) * D;
-                return true;
-            });
-            stage_vt<D, BF16>(Vt, v, (((size_t)b * T_ + kb0) * Hkv + g) * D, (size_t)Hkv * D, 64);
-            __syncthreads();
-            attend64<D, BF16>(Qs + wave * 16 * T::QS, Ks, Vt, sl2, kb0, tq, o, m, l);
+        if (blk < 0) return -1;
+        const int kb0 = blk * BETA + sub * 64;
+        return kb0 > t0 + 63 ? -1 : kb0;
+    };
+    auto next_item = [&](int &j, int &sub) {   // advance to the next present item
+        for (;;) {
+            if (++sub == BETA / 64) { sub = 0; ++j; }
+            if (j >= nblk || item_key0(j, sub) >= 0) return;
         }
+    };
+    int j = 0, sub = 0;
+    if (nblk > 0 && item_key0(0, 0) < 0) next_item(j, sub);
+    RowStager<D, BF16> kst;
+    VtStager<D, BF16> vst;
+    auto issue_kv = [&](int kb0) {
+        kst.issue(k_rot, [&](int r, size_t &off) {
+            off = (((size_t)b * T_ + kb0 + r) * Hkv + g) * D;
+            return true;
+        });
+        vst.issue(v, (((size_t)b * T_ + kb0) * Hkv + g) * D, (size_t)Hkv * D);
+    };
+    int kb_cur = j < nblk ? item_key0(j, sub) : -1;
+    if (kb_cur >= 0) issue_kv(kb_cur);
+    Frag8<BF16> qf[D / 32];
+    qst.get(qf);
+    if (kb_cur >= 0) {
+        kst.commit(Ks);
+        vst.commit(Vt);
+    }
+    __syncthreads();
+    while (kb_cur >= 0) {
+        int jn = j, sn = sub;
+        next_item(jn, sn);
+        const int kb_next = jn < nblk ? item_key0(jn, sn) : -1;
+        if (kb_next >= 0) issue_kv(kb_next);   // in flight during this compute
+        attend64<D, BF16>(qf, Ks, Vt, sl2, kb_cur, tq, o, m, l);
+        __syncthreads();
+        if (kb_next >= 0) {
+            kst.commit(Ks);
+            vst.commit(Vt);
+            __syncthreads();
+        }
+        j = jn;
+        sub = sn;
+        kb_cur = kb_next;
     }
 
     // merge: local (and shared) part, then the remote partials in slot order
-    const long route = route0 + wave * 16 + lr;
-    float lse = m + log2f(l);
-    float inv = 1.0f / l;
+    const float lse = m + __builtin_amdgcn_logf(l);
+    const float inv = 1.0f / l;
     float acc[D / 16][4];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
@@ -453,18 +691,20 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const void *__restr
         for (int r = 0; r < 4; ++r) acc[dt][r] = o[dt][r] * inv;
     if (!uni) {
         const int32_t *ep = entry_pos + route * R;
+        auto ep_at = [&](int r) { return r < RP ? ep_pre[r] : ep[r]; };
+        auto lse_at = [&](int r) { return r < RP ? lse_pre[r] : part_lse[ep[r]]; };
         float M = lse;
         for (int r = 0; r < R; ++r)
-            if (ep[r] >= 0) M = fmaxf(M, part_lse[route * R + r]);
-        float wsum = exp2f(lse - M);
+            if (ep_at(r) >= 0) M = fmaxf(M, lse_at(r));
+        float wsum = __builtin_amdgcn_exp2f(lse - M);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[dt][r] *= wsum;
         for (int r = 0; r < R; ++r) {
-            if (ep[r] < 0) continue;
-            const long e = route * R + r;
-            const float w = exp2f(part_lse[e] - M);
+            if (ep_at(r) < 0) continue;
+            const long e = ep_at(r);
+            const float w = __builtin_amdgcn_exp2f(lse_at(r) - M);
             wsum += w;
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
@@ -480,9 +720,10 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const void *__restr
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[dt][r] *= iw;
     }
-    E *op = reinterpret_cast<E *>(out) + (((size_t)b * T_ + tq) * Hq + h) * D;
+    E *op = out + (((size_t)b * T_ + tq) * Hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) store4(op + dt * 16 + 4 * lg, acc[dt]);
+    }
 }
 
 template <typename F>
@@ -492,11 +733,34 @@ hipError_t ensure_lds(F *fn, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// Workgroups for a persistent launch: as many as fit on the device at once
+// (occupancy of `fn` at 256 threads and `lds` bytes), at most `items`.
+template <typename F>
+unsigned persistent_grid(F *fn, size_t lds, long items) {
+    int dev = 0, cus = 256, per_cu = 1;
+    if (hipGetDevice(&dev) == hipSuccess)
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn),
+                                                     256, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const long g = (long)cus * per_cu;
+    return (unsigned)std::max(1L, std::min(items, g));
+}
+
 struct AttnWs {
-    int32_t *count, *bin_start, *chunk_start, *total, *tile_flag, *entry_pos, *list;
+    int32_t *cnt, *seg_rel, *bin_local, *chunk_local, *wg_sum, *chunk_bin, *tile_flag,
+        *entry_pos, *list, *list_q;
     float *part_lse;
-    void *part_o;
+    void *part_o, *q_rot, *k_rot;
 };
+
+int num_segments(const Shape &s) { return (s.T + SEG - 1) / SEG; }
+
+long max_chunks(const Shape &s) {
+    const long nbins = (long)s.B * s.Hkv * s.NB;
+    const long nent = (long)s.B * s.Hq * s.T * s.R;
+    return nbins + (nent + CHUNK_ROWS - 1) / CHUNK_ROWS;
+}
 
 template <int D, int BETA, bool BF16>
 hipError_t run_attention(const Shape &s, const void *q, const void *k, const void *v,
@@ -505,30 +769,45 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     using T = Tile<D, BF16>;
     using E = Elem<BF16>;
     const int nbins = s.B * s.Hkv * s.NB;
+    const int nseg = num_segments(s);
+    const int nwg = (nbins + BIN_WG - 1) / BIN_WG;
     const long ntiles = (long)s.B * s.Hq * (s.T / 64);
     const long nent = (long)s.B * s.Hq * s.T * s.R;
-    k_fill_i32<<<dim3((unsigned)((nbins + 255) / 256)), 256, 0, st>>>(w.count, nbins, 0);
-    k_attn_plan<<<dim3((unsigned)((ntiles + 3) / 4)), 256, 0, st>>>(s, sel, w.count, w.entry_pos,
-                                                                     w.tile_flag);
-    k_attn_scan<<<1, SCAN_THREADS, 0, st>>>(nbins, w.count, w.bin_start, w.chunk_start, w.total);
-    k_attn_scatter<<<dim3((unsigned)((nent + 255) / 256)), 256, 0, st>>>(s, sel, w.entry_pos,
-                                                                         w.bin_start, w.list);
-    hipError_t err = hipGetLastError();
+    const long rot_tasks = (long)s.B * s.T * (s.Hq + s.Hkv) * (D / 8);
+    k_attn_rotate<D, BF16><<<dim3((unsigned)std::min<long>((rot_tasks + 255) / 256, 65536L)), 256, 0,
+                             st>>>(s, q, k, cos_t, sin_t, reinterpret_cast<E *>(w.q_rot),
+                                   reinterpret_cast<E *>(w.k_rot));
+    hipError_t err = ensure_lds(k_attn_prep, (size_t)s.NB * sizeof(int));
     if (err != hipSuccess) return err;
-    const long max_chunks = nbins + (nent + CHUNK_ROWS - 1) / CHUNK_ROWS;
-    const size_t lds_r = (size_t)((BETA / 64) * (T::K_ELEMS + T::V_ELEMS) + T::Q_ELEMS) * sizeof(E);
+    k_attn_prep<<<dim3((unsigned)nseg, (unsigned)s.Hkv, (unsigned)s.B), 256,
+                  (size_t)s.NB * sizeof(int), st>>>(s, sel, w.cnt, w.entry_pos, w.tile_flag, nseg);
+    k_attn_binsum<<<dim3((unsigned)nwg), BIN_WG, 0, st>>>(nbins, nseg, w.cnt, w.seg_rel,
+                                                          w.bin_local, w.chunk_local, w.wg_sum);
+    k_attn_scan<<<1, 1024, 0, st>>>(nwg, w.wg_sum);
+    const long nscat = std::max<long>(nent, nbins);
+    k_attn_scatter<<<dim3((unsigned)((nscat + 255) / 256)), 256, 0, st>>>(
+        s, nseg, nbins, sel, w.entry_pos, w.bin_local, w.chunk_local, w.wg_sum, w.seg_rel, w.list,
+        w.list_q, w.chunk_bin);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const size_t lds_r = (size_t)((BETA / 64) * (T::K_ELEMS + T::V_ELEMS)) * sizeof(E);
     err = ensure_lds(k_attn_remote<D, BETA, BF16>, lds_r);
     if (err != hipSuccess) return err;
-    k_attn_remote<D, BETA, BF16><<<dim3((unsigned)max_chunks), 256, lds_r, st>>>(
-        s, q, k, v, cos_t, sin_t, w.list, w.bin_start, w.chunk_start, w.total, w.part_lse,
-        reinterpret_cast<E *>(w.part_o));
-    const size_t lds_l = (size_t)(T::Q_ELEMS + T::K_ELEMS + T::V_ELEMS) * sizeof(E) +
+    const unsigned grid_r = persistent_grid(k_attn_remote<D, BETA, BF16>, lds_r, max_chunks(s));
+    k_attn_remote<D, BETA, BF16><<<dim3(grid_r), 256, lds_r, st>>>(
+        s, reinterpret_cast<const E *>(w.q_rot), reinterpret_cast<const E *>(w.k_rot),
+        reinterpret_cast<const E *>(v), w.list, w.list_q, w.bin_local, w.chunk_local, w.wg_sum,
+        w.chunk_bin,
+        nbins, w.part_lse, reinterpret_cast<E *>(w.part_o));
+    const size_t lds_l = (size_t)(T::K_ELEMS + T::V_ELEMS) * sizeof(E) +
                          (size_t)s.R * sizeof(int);
     err = ensure_lds(k_attn_local<D, BETA, BF16>, lds_l);
     if (err != hipSuccess) return err;
-    k_attn_local<D, BETA, BF16><<<dim3((unsigned)ntiles), 256, lds_l, st>>>(
-        s, q, k, v, cos_t, sin_t, sel, w.tile_flag, w.entry_pos, w.part_lse,
-        reinterpret_cast<const E *>(w.part_o), out);
+    const unsigned grid_l = persistent_grid(k_attn_local<D, BETA, BF16>, lds_l, ntiles);
+    k_attn_local<D, BETA, BF16><<<dim3(grid_l), 256, lds_l, st>>>(
+        s, reinterpret_cast<const E *>(w.q_rot), reinterpret_cast<const E *>(w.k_rot),
+        reinterpret_cast<const E *>(v), sel, w.tile_flag, w.entry_pos, w.part_lse,
+        reinterpret_cast<const E *>(w.part_o), reinterpret_cast<E *>(out));
     return hipGetLastError();
 }
 
@@ -538,38 +817,50 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
 size_t attention_ws_layout(const Shape &s, size_t *off) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t nbins = (size_t)s.B * s.Hkv * s.NB;
+    const size_t nseg = (size_t)num_segments(s);
+    const size_t nwg = (nbins + BIN_WG - 1) / BIN_WG;
     const size_t ntiles = (size_t)s.B * s.Hq * (s.T / 64);
     const size_t nent = (size_t)s.B * s.Hq * s.T * s.R;
     const size_t esz = s.dtype == 1 ? 2 : 4;
     size_t p = 0;
-    off[0] = p; p = al(p + nbins * 4);              // count
-    off[1] = p; p = al(p + (nbins + 1) * 4);        // bin_start
-    off[2] = p; p = al(p + (nbins + 1) * 4);        // chunk_start
-    off[3] = p; p = al(p + 4);                      // total chunks
-    off[4] = p; p = al(p + ntiles * 4);             // tile flags
-    off[5] = p; p = al(p + nent * 4);               // entry positions
-    off[6] = p; p = al(p + nent * 4);               // list
-    off[7] = p; p = al(p + nent * 4);               // partial lse
-    off[8] = p; p = al(p + nent * (size_t)s.d * esz);  // partial outputs
+    off[0] = p; p = al(p + nbins * nseg * 4);                 // per-segment bin counts
+    off[1] = p; p = al(p + nbins * nseg * 4);                 // segment offsets in bins
+    off[2] = p; p = al(p + nbins * 4);                        // bin start within workgroup
+    off[3] = p; p = al(p + nbins * 4);                        // chunk start within workgroup
+    off[4] = p; p = al(p + (2 * nwg + 2) * 4);                // workgroup bases and totals
+    off[5] = p; p = al(p + (size_t)max_chunks(s) * 4);        // chunk -> bin
+    off[6] = p; p = al(p + ntiles * 4);                       // tile flags
+    off[7] = p; p = al(p + nent * 4);                         // entry ranks
+    off[8] = p; p = al(p + nent * 4);                         // list
+    off[9] = p; p = al(p + nent * 4);                         // partial lse
+    off[10] = p; p = al(p + nent * (size_t)s.d * esz);        // partial outputs
+    off[11] = p; p = al(p + (size_t)s.B * s.T * s.Hq * s.d * esz);   // rotated q
+    off[12] = p; p = al(p + (size_t)s.B * s.T * s.Hkv * s.d * esz);  // rotated k
+    off[13] = p; p = al(p + nent * 4);                        // q rows of the list
     return p;
 }
 
 hipError_t launch_attention(const Shape &s, const void *q, const void *k, const void *v,
                             const float *cos_t, const float *sin_t, const int32_t *sel, void *out,
                             void *ws, hipStream_t st) {
-    size_t off[9];
+    size_t off[14];
     attention_ws_layout(s, off);
     unsigned char *base = reinterpret_cast<unsigned char *>(ws);
     AttnWs w;
-    w.count = reinterpret_cast<int32_t *>(base + off[0]);
-    w.bin_start = reinterpret_cast<int32_t *>(base + off[1]);
-    w.chunk_start = reinterpret_cast<int32_t *>(base + off[2]);
-    w.total = reinterpret_cast<int32_t *>(base + off[3]);
-    w.tile_flag = reinterpret_cast<int32_t *>(base + off[4]);
-    w.entry_pos = reinterpret_cast<int32_t *>(base + off[5]);
-    w.list = reinterpret_cast<int32_t *>(base + off[6]);
-    w.part_lse = reinterpret_cast<float *>(base + off[7]);
-    w.part_o = base + off[8];
+    w.cnt = reinterpret_cast<int32_t *>(base + off[0]);
+    w.seg_rel = reinterpret_cast<int32_t *>(base + off[1]);
+    w.bin_local = reinterpret_cast<int32_t *>(base + off[2]);
+    w.chunk_local = reinterpret_cast<int32_t *>(base + off[3]);
+    w.wg_sum = reinterpret_cast<int32_t *>(base + off[4]);
+    w.chunk_bin = reinterpret_cast<int32_t *>(base + off[5]);
+    w.tile_flag = reinterpret_cast<int32_t *>(base + off[6]);
+    w.entry_pos = reinterpret_cast<int32_t *>(base + off[7]);
+    w.list = reinterpret_cast<int32_t *>(base + off[8]);
+    w.part_lse = reinterpret_cast<float *>(base + off[9]);
+    w.part_o = base + off[10];
+    w.q_rot = base + off[11];
+    w.k_rot = base + off[12];
+    w.list_q = reinterpret_cast<int32_t *>(base + off[13]);
     const bool bf = s.dtype == 1;
 #define MONO_ATTN_ARGS s, q, k, v, cos_t, sin_t, sel, out, w, st
     if (s.d == 64) {

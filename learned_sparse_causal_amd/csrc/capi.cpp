@@ -101,7 +101,7 @@ size_t mixer_layout(const Shape &s, size_t *off) {
     off[9] = p; p = al256(p + BT * s.Hq * s.R * 4);
     off[10] = p; p = al256(p + BT * s.Hq * s.d * es);
     off[11] = p;
-    size_t aoff[9];
+    size_t aoff[14];
     p += attention_ws_layout(s, aoff);
     return p;
 }
@@ -120,7 +120,7 @@ size_t mono_workspace_bytes(const mono_config *cfg, int which) {
     Shape s;
     const bool mixer = which == MONO_WS_MIXER;
     if (make_shape(cfg, mixer, s) != MONO_OK) return 0;
-    size_t off[12];
+    size_t off[14];
     switch (which) {
         case MONO_WS_BUILD:
         case MONO_WS_ROUTE:
@@ -188,7 +188,7 @@ mono_status mono_selected_attention(const mono_config *cfg, const void *q, const
     const mono_status st = make_shape(cfg, false, s);
     if (st != MONO_OK) return st;
     if (!q || !k || !v || !rope_cos || !rope_sin || !sel || !out || !ws) return MONO_ERR_NULL;
-    size_t off[9];
+    size_t off[14];
     if (ws_bytes < attention_ws_layout(s, off)) return MONO_ERR_WORKSPACE;
     return hip_status(launch_attention(s, q, k, v, rope_cos, rope_sin, sel, out, ws,
                                        reinterpret_cast<hipStream_t>(stream)));

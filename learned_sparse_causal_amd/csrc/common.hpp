@@ -21,11 +21,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(u16 b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// Round to nearest bfloat16, ties to even (finite inputs).
+// Round to nearest bfloat16, ties to even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ u16 f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (u16)(u >> 16);
+    return __builtin_bit_cast(u16, (__bf16)f);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bfloat16 pair (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2_t x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
 
 // Load 8 consecutive activations starting at element i (16-byte aligned for

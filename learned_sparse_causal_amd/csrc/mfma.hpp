@@ -71,10 +71,10 @@ __device__ __forceinline__ Frag8<false> lds_frag4x2(const float *p0, const float
 // Fragment from 8 floats in registers (rounded to bf16 for the bf16 path).
 __device__ __forceinline__ Frag8<true> reg_frag8_bf16(const float *x) {
     uint4 w;
-    w.x = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-    w.y = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
-    w.z = (uint32_t)f32_to_bf16_bits(x[4]) | ((uint32_t)f32_to_bf16_bits(x[5]) << 16);
-    w.w = (uint32_t)f32_to_bf16_bits(x[6]) | ((uint32_t)f32_to_bf16_bits(x[7]) << 16);
+    w.x = pack_bf16x2(x[0], x[1]);
+    w.y = pack_bf16x2(x[2], x[3]);
+    w.z = pack_bf16x2(x[4], x[5]);
+    w.w = pack_bf16x2(x[6], x[7]);
     Frag8<true> f;
     f.v = __builtin_bit_cast(bf16x8, w);
     return f;
