@@ -5,15 +5,21 @@ One step = mono_build_index + mono_route + mono_selected_attention over one
 batch of synthetic q, k, v already resident in HBM (the scaling-sweep
 workload at T = 32768: batch 1, 16 heads, d 64, block 64, 1024 addresses,
 capacity 64, 4 probes, R = 2 remote + 2 local blocks, bf16).  Prints one JSON
-line: tokens/s, the dominant kernel's roofline, and the CPU oracle timed on a
-bounded sample on the host cores.
+line: tokens/s, the dominant kernel's roofline (its duration taken from HIP
+events recorded around its launches inside the timed steps), the per-stage
+floors, the 4K-32K sweep exponent and the CPU oracle timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-cpu-baseline]
+                    [--copy-calibration]
+
+--copy-calibration runs a plain 256 MiB device copy before the steps; hardware
+counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes.
 """
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -25,23 +31,32 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 FP32_VECTOR_TFLOPS = 157.3       # MI355X fp32 vector peak
 BF16_MFMA_TFLOPS = 2500.0        # MI355X dense bf16 MFMA peak
+COPY_BYTES = 256 << 20
+
+# Hardware-counter traffic of a kernel, kept as a short text summary with the
+# sha256 of the source it was measured on (a changed source voids it).
+TRAFFIC_FILES = {"k_route": ("profiles/k_route_sweep_T32768_traffic.md",
+                             "learned_sparse_causal_amd/csrc/route.hip")}
 
 
 def workload_bytes_flops(cfg, sel_np=None):
     """Algorithmic bytes and flops of each stage for one step (what the method
-    must move or compute), per the per-unit figures in the design doc."""
+    must move or compute)."""
     es = 2 if cfg.dtype == "bf16" else 4
     B, T, Hq, Hkv, d, R = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.d, cfg.R
     NB = cfg.NB
+    # build: read k once; write the summaries, addresses and the lists
     build_bytes = B * T * Hkv * d * es + B * Hkv * NB * (4 * d + 4 + 4) + \
         B * Hkv * (2 * cfg.A + 2) * 4
     t = np.arange(T)
     qb = t // cfg.beta
     E = np.maximum(0, qb - cfg.L + 1)
-    searched = (E > R).sum()
-    route_bytes = B * Hq * searched * d * es + B * Hq * T * R * 4
-    route_flops = B * Hq * searched * (2 * cfg.K * d + 2 * R * d)
-    # attended keys per query: selected remote tokens + local tokens <= t
+    searched = int((E > R).sum()) * B * Hq
+    # route: read q of every searched query once, write R ids per route;
+    # per searched route K*d MACs (codebook scores), A adds (address sums),
+    # R*d MACs (rerank of at least R candidates)
+    route_bytes = searched * d * es + B * Hq * T * R * 4
+    route_flops = searched * (2 * cfg.K * d + cfg.A + 2 * R * d)
     lo = np.maximum(0, qb - cfg.L + 1) * cfg.beta
     local = t - lo + 1
     if sel_np is not None:
@@ -52,10 +67,24 @@ def workload_bytes_flops(cfg, sel_np=None):
     attn_flops = 4.0 * d * keys
     attn_bytes = (B * T * Hq * d * es) * 2 + 2 * B * T * Hkv * d * es + B * Hq * T * R * 4
     return dict(build_bytes=build_bytes, route_bytes=route_bytes, route_flops=route_flops,
-                attn_bytes=attn_bytes, attn_flops=attn_flops)
+                attn_bytes=attn_bytes, attn_flops=attn_flops, searched_routes=searched)
 
 
-def run_gpu(cfg, steps, warmup, per_stage=True):
+def copy_calibration():
+    """A plain device copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES),
+    three launches: the reference for the hardware byte counters."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def run_gpu(cfg, steps, warmup):
+    """Times `steps` steps between two synchronizations; HIP events recorded on
+    the launch stream around every stage of every timed step give the
+    per-stage (and, for route, per-kernel) device durations."""
     import torch
     from learned_sparse_causal_amd import binding, synth
     d = synth.qkv_device(cfg)
@@ -78,59 +107,60 @@ def run_gpu(cfg, steps, warmup, per_stage=True):
 
     for _ in range(warmup):
         step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
-    # whole-step timing: exactly `steps` steps between two synchronizations
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
+    for e in evs:
+        step(e)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    stage = None
-    if per_stage:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-        for e in evs:
-            step(e)
-        torch.cuda.synchronize()
-        stage = {k: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
-                 for i, k in enumerate(("build", "route", "attend"))}
-    stats = dict(overflow=int(idx["overflow"].sum().item()), max_load=int(idx["load"].max().item()))
-    return wall_ms, stage, stats, sel
+    step_us = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+    stage = {k: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
+             for i, k in enumerate(("build", "route", "attend"))}
+    stats = dict(overflow=int(idx["overflow"].sum().item()), max_load=int(idx["load"].max().item()),
+                 mean_load=float(cfg.NB / cfg.A))
+    return wall_ms, stage, step_us, stats, sel
 
 
-def cpu_baseline(cfg, budget_s=15.0):
-    """The oracle (as it stands) on the host: the whole index build, then route
-    + attention for a random sample of routes sized to the time budget; the
-    full-step time is extrapolated from the per-route rate."""
+def measured_traffic(kernel):
+    """Bytes per launch from the committed counter summary, or None if there is
+    none or the kernel's source changed since it was taken."""
+    if kernel not in TRAFFIC_FILES:
+        return None
+    summary, src = (os.path.join(ROOT, p) for p in TRAFFIC_FILES[kernel])
+    if not os.path.exists(summary):
+        return None
+    text = open(summary).read()
+    m_sha = re.search(r"source sha256: ([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic bytes per launch: ([0-9.eE+]+)", text)
+    if not (m_sha and m_val):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return float(m_val.group(1)) if sha == m_sha.group(1) else None
+
+
+def cpu_baseline(cfg, reps=3):
+    """The oracle (as it stands) on the host cores: the whole step (index
+    build, route and attention of every query) run `reps` times, median."""
     import oracle
     from learned_sparse_causal_amd import synth
     oracle.build_oracle(force=False)
-    threads = min(16, os.cpu_count() or 1)
+    threads = min(16, oracle.max_threads())
     inp = synth.qkv(cfg)
     c, s = oracle.rope_table(cfg.T, cfg.d)
     sh = oracle.Shape.of(**cfg.shape_kw())
-    t0 = time.perf_counter()
-    idx = oracle.build_index(sh, inp["k"], c, s, inp["codebooks"], threads)
-    t_build = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    n = 2000
-    spent, done = 0.0, 0
-    while True:
-        ids = rng.choice(cfg.routes, size=n, replace=False).astype(np.int64)
+    times = []
+    for _ in range(reps):
         t0 = time.perf_counter()
-        sel, _ = oracle.route(sh, inp["q"], c, s, inp["codebooks"], idx, ids, threads)
-        oracle.attention(sh, inp["q"], inp["k"], inp["v"], c, s, sel, ids, threads)
-        dt = time.perf_counter() - t0
-        spent += dt
-        done += n
-        if spent + t_build > budget_s * 0.5 or done >= cfg.routes:
-            break
-        n = min(cfg.routes, int(n * max(2.0, (budget_s * 0.5 - t_build) / max(dt, 1e-3))))
-    per_route = spent / done
-    t_step = t_build + per_route * cfg.routes
+        idx = oracle.build_index(sh, inp["k"], c, s, inp["codebooks"], threads)
+        sel, _ = oracle.route(sh, inp["q"], c, s, inp["codebooks"], idx, None, threads)
+        oracle.attention(sh, inp["q"], inp["k"], inp["v"], c, s, sel, None, threads)
+        times.append(time.perf_counter() - t0)
+    t_step = float(np.median(times))
     return dict(value=cfg.B * cfg.T / t_step, unit="tokens/s", cores=threads, kind="oracle",
-                sample="full index build (%.2f s) + route and attention of %d random routes of "
-                       "%d (%.2f s), full step extrapolated from the per-route rate: %.1f s"
-                       % (t_build, done, cfg.routes, spent, t_step))
+                sample="the whole step (index build, route and fp64 attention of all %d queries, "
+                       "numpy-drawn inputs of the same distribution), %d runs, median %.2f s"
+                       % (cfg.routes, reps, t_step))
 
 
 def main():
@@ -140,19 +170,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the routed attention path is built and timed on a "
-              "single MI355X (--gpus 1); multi-GPU runs are not part of this build.",
+              "single MI355X (--gpus 1); runs on several GPUs are not supported.",
               file=sys.stderr)
         sys.exit(2)
     from learned_sparse_causal_amd import configs
 
+    if args.copy_calibration:
+        copy_calibration()
     cfg = configs.SWEEP_32K
-    wall_ms, stage, stats, sel = run_gpu(cfg, args.steps, args.warmup)
+    wall_ms, stage, step_us, stats, sel = run_gpu(cfg, args.steps, args.warmup)
     w = workload_bytes_flops(cfg, sel.cpu().numpy())
     tokens = cfg.B * cfg.T
-    # per-stage roofline floors and the dominant stage
     floors = {
         "build": w["build_bytes"] / (HBM_PEAK_GBS * 1e9),
         "route": max(w["route_bytes"] / (HBM_PEAK_GBS * 1e9),
@@ -160,21 +192,15 @@ def main():
         "attend": max(w["attn_bytes"] / (HBM_PEAK_GBS * 1e9),
                       w["attn_flops"] / (BF16_MFMA_TFLOPS * 1e12)),
     }
-    dom = max(stage, key=stage.get)
-    t_dom = stage[dom] * 1e-6
-    if dom == "route":
-        roof = dict(bound="alu", achieved=w["route_flops"] / t_dom / 1e12,
-                    peak=FP32_VECTOR_TFLOPS, unit="TFLOP/s")
-    elif dom == "build":
-        roof = dict(bound="hbm", achieved=w["build_bytes"] / t_dom / 1e9, peak=HBM_PEAK_GBS,
-                    unit="GB/s")
-    else:
-        roof = dict(bound="hbm", achieved=w["attn_bytes"] / t_dom / 1e9, peak=HBM_PEAK_GBS,
-                    unit="GB/s")
+    # the dominant single kernel is the router (mono_route launches k_route only)
+    t_route = stage["route"] * 1e-6
+    roof = dict(bound="alu", achieved=w["route_flops"] / t_route / 1e12,
+                peak=FP32_VECTOR_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = {"route": "k_route", "build": "k_block_address+k_posting_lists",
-                      "attend": "mono_selected_attention (6 kernels)"}[dom]
+    roof["traffic"] = measured_traffic("k_route")
+    roof["kernel"] = "k_route"
+    roof["kernel_us"] = stage["route"]
+    roof["hbm_GBs"] = w["route_bytes"] / t_route / 1e9
     line = dict(
         metric="routed-attn tokens/s (build+route+attend) at T=32K; % HBM/MFMA roofline",
         value=tokens / (wall_ms * 1e-3), unit="tokens/s", n_gpus=1, steps=args.steps,
@@ -185,6 +211,7 @@ def main():
                     R=cfg.R, L=cfg.L),
         roofline=roof,
         stage_us=stage,
+        step_us_spread=dict(min=min(step_us), median=float(np.median(step_us)), max=max(step_us)),
         path_roofline_frac=sum(floors.values()) / (wall_ms * 1e-3),
         floors_us={k: v * 1e6 for k, v in floors.items()},
         index=stats,
@@ -192,12 +219,8 @@ def main():
     if not args.no_sweep:
         pts = []
         for T in configs.SWEEP_T:
-            c = configs.sweep(T)
-            times = []
-            for _ in range(3):
-                ms, _, _, _ = run_gpu(c, 1, 1, per_stage=False)
-                times.append(ms)
-            pts.append((T, float(np.median(times))))
+            _, _, us, _, _ = run_gpu(configs.sweep(T), 3, 1)
+            pts.append((T, float(np.median(us)) * 1e-3))
         x = np.log([p[0] for p in pts])
         y = np.log([p[1] for p in pts])
         line["sweep"] = dict(points_ms={str(T): ms for T, ms in pts},
