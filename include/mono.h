@@ -34,7 +34,7 @@
  * block_size 64 or 128; n_components 1 or 2; codes_per_component 2..64 (so
  * at most 4096 addresses); 1 <= n_probes <= 16; n_remote <= 16 unless every
  * query bypasses the search (n_remote >= seq_len/block_size - n_local);
- * seq_len/block_size <= 8192.
+ * seq_len/block_size <= 8192; n_kv_heads * head_dim <= 4096.
  */
 #ifndef MONO_H
 #define MONO_H

@@ -22,103 +22,185 @@
 
 namespace {
 
-// One wave handles 64 / (d/2) (block, kv-head) tasks: 2 for d = 64, 1 for d = 128.
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void k_block_address(Shape s, const void *__restrict__ k,
-                                                       const float *__restrict__ cos_t,
-                                                       const float *__restrict__ sin_t,
-                                                       const float *__restrict__ cb,
-                                                       float *__restrict__ kbar,
-                                                       int32_t *__restrict__ addr) {
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BA_THREADS = 256;
+constexpr int BA_CHUNK_BYTES = 32768;   // LDS staging of key rows per chunk
+
+// Tokens per staged chunk: the largest power of two dividing the block size
+// whose rows (all kv-heads) fit in BA_CHUNK_BYTES and whose rotary-table
+// entries (d/2 per token) fit the per-thread staging registers.
+int block_chunk_tokens(const Shape &s) {
+    const int row = s.Hkv * s.d * (s.dtype == 1 ? 2 : 4);
+    const int tab_max = BA_CHUNK_BYTES / 16;     // VPT * BA_THREADS
+    int ct = s.beta;
+    while (ct > 1 && (ct * row > BA_CHUNK_BYTES || ct * (s.d / 2) > tab_max)) ct /= 2;
+    return ct;
+}
+
+size_t block_address_lds(const Shape &s, int ct) {
+    const int es = s.dtype == 1 ? 2 : 4;
+    return (size_t)ct * s.Hkv * s.d * es          // key rows
+           + (size_t)2 * ct * (s.d / 2) * 4       // cos, sin rows
+           + (size_t)s.Hkv * s.d * 4              // summaries
+           + (size_t)s.Hkv * s.P * s.K * 4;       // code scores
+}
+
+// One workgroup per (batch, block n).  The block's key rows (every kv-head)
+// pass through LDS in chunks of CT tokens, read with 16-byte loads; the next
+// chunk's loads are in flight while the current chunk is summed.  Thread slot
+// j of thread x owns rotation pair x + 256 j, i.e. kv-head g and dims
+// (i, i + d/2), and sums it over the tokens in order (fp32, products rounded
+// before the add, as the rotation is defined).  Then one thread per
+// (kv-head, code) scores the summary with an fp32 fused multiply-add chain
+// in dimension order and one thread per kv-head takes the argmax of every
+// component (lowest code on ties) and writes the address.  MAXP bounds the
+// pairs per thread (Hkv d / 2 <= 256 MAXP).
+template <int D, int P, bool BF16, int MAXP>
+__global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT,
+                                                              const void *__restrict__ k,
+                                                              const float *__restrict__ cos_t,
+                                                              const float *__restrict__ sin_t,
+                                                              const float *__restrict__ cb,
+                                                              float *__restrict__ kbar,
+                                                              int32_t *__restrict__ addr) {
     constexpr int H = D / 2;
-    constexpr int TPW = WAVE / H;                 // tasks per wave
-    __shared__ float kb_s[4][TPW][D];
-    __shared__ float sc_s[4][TPW][128];
-    __shared__ int code_s[4][TPW][2];
+    constexpr int DS = D / P;
+    constexpr int ES = BF16 ? 2 : 4;
+    constexpr int VPT = BA_CHUNK_BYTES / 16 / BA_THREADS;      // 16-byte loads per thread
+    extern __shared__ __align__(16) char ba_lds[];
+    const int Hkv = s.Hkv, K = s.K, PK = P * K;
+    const int rowE = Hkv * D;                                   // elements per token row
+    char *rows = ba_lds;                                        // [CT][rowE]
+    float *cs = reinterpret_cast<float *>(ba_lds + (size_t)CT * rowE * ES);   // [CT][H]
+    float *sn = cs + CT * H;                                    // [CT][H]
+    float *kb = sn + CT * H;                                    // [Hkv][D]
+    float *sc = kb + Hkv * D;                                   // [Hkv][PK]
 
-    const int lane = lane_id(), wave = threadIdx.x / WAVE;
-    const int sub = lane / H, i = lane % H;
-    const long ntask = (long)s.B * s.NB * s.Hkv;
-    const long task = ((long)blockIdx.x * 4 + wave) * TPW + sub;
-    const bool live = task < ntask;
-    // task order (b, n, g): the heads of one block are neighbours and share
-    // the rotary table rows in cache.
-    const long tt = live ? task : 0;
-    const int g = (int)(tt % s.Hkv);
-    const int n = (int)((tt / s.Hkv) % s.NB);
-    const int b = (int)(tt / ((long)s.Hkv * s.NB));
+    const int tid = threadIdx.x;
+    const int n = blockIdx.x, b = blockIdx.y;
+    const int t0 = n * s.beta;
+    const int npairs = Hkv * H;
+    const int vecs = CT * rowE * ES / 16;                       // 16-byte vectors per chunk
+    const int tabs = CT * H;                                    // table entries per chunk
+    const char *kbase = reinterpret_cast<const char *>(k) + ((size_t)b * s.T + t0) * rowE * ES;
 
-    float acc0 = 0.0f, acc1 = 0.0f;
-    const int beta = s.beta;
-    const size_t row_stride = (size_t)s.Hkv * D;
-    const size_t base = (((size_t)b * s.T + (size_t)n * beta) * s.Hkv + g) * D;
-    if (live) {
+    float a0[MAXP], a1[MAXP];
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) { a0[j] = 0.0f; a1[j] = 0.0f; }
+
+    // staging registers; indexes are clamped so every thread loads in bounds
+    // and only the threads that own a vector store it
+    u32x4 tmp[VPT];
+    float tc[VPT], ts[VPT];
+#define MONO_BA_FETCH(c_)                                                                  \
+    {                                                                                      \
+        const u32x4 *src_ = reinterpret_cast<const u32x4 *>(kbase + (size_t)(c_)*rowE * ES); \
+        const float *cg_ = cos_t + (size_t)(t0 + (c_)) * H;                                \
+        const float *sg_ = sin_t + (size_t)(t0 + (c_)) * H;                                \
+        _Pragma("clang loop unroll(full)") for (int j = 0; j < VPT; ++j) {                  \
+            const int v = tid + j * BA_THREADS;                                            \
+            tmp[j] = src_[min(v, vecs - 1)];                                               \
+            tc[j] = cg_[min(v, tabs - 1)];                                                 \
+            ts[j] = sg_[min(v, tabs - 1)];                                                 \
+        }                                                                                  \
+    }
+    MONO_BA_FETCH(0)
+    for (int c = 0; c < s.beta; c += CT) {
+#pragma clang loop unroll(full)
+        for (int j = 0; j < VPT; ++j) {
+            const int v = tid + j * BA_THREADS;
+            if (v < vecs) reinterpret_cast<u32x4 *>(rows)[v] = tmp[j];
+        }
+#pragma clang loop unroll(full)
+        for (int j = 0; j < VPT; ++j) {
+            const int v = tid + j * BA_THREADS;
+            if (v < tabs) { cs[v] = tc[j]; sn[v] = ts[j]; }
+        }
+        __syncthreads();
+        if (c + CT < s.beta) MONO_BA_FETCH(c + CT)
+#pragma unroll
+        for (int j = 0; j < MAXP; ++j) {
+            const int pr = tid + j * BA_THREADS;
+            if (pr < npairs) {
+                const int g = pr / H, i = pr - g * H;
 #pragma unroll 8
-        for (int u = 0; u < beta; ++u) {
-            const int t = n * beta + u;
-            const size_t r = base + (size_t)u * row_stride;
-            const float x0 = load1<BF16>(k, r + i);
-            const float x1 = load1<BF16>(k, r + i + H);
-            const float c = cos_t[(size_t)t * H + i];
-            const float sn = sin_t[(size_t)t * H + i];
-            const float p0 = x0 * c, p1 = x1 * sn, p2 = x1 * c, p3 = x0 * sn;
-            acc0 = acc0 + (p0 - p1);
-            acc1 = acc1 + (p2 + p3);
+                for (int u = 0; u < CT; ++u) {
+                    const int e = u * rowE + g * D + i;
+                    float x0, x1;
+                    if constexpr (BF16) {
+                        x0 = bf16_bits_to_f32(reinterpret_cast<const u16 *>(rows)[e]);
+                        x1 = bf16_bits_to_f32(reinterpret_cast<const u16 *>(rows)[e + H]);
+                    } else {
+                        x0 = reinterpret_cast<const float *>(rows)[e];
+                        x1 = reinterpret_cast<const float *>(rows)[e + H];
+                    }
+                    const float cc = cs[u * H + i], ss = sn[u * H + i];
+                    const float p0 = x0 * cc, p1 = x1 * ss, p2 = x1 * cc, p3 = x0 * ss;
+                    a0[j] = a0[j] + (p0 - p1);
+                    a1[j] = a1[j] + (p2 + p3);
+                }
+            }
+        }
+        __syncthreads();
+    }
+#undef MONO_BA_FETCH
+
+    // summaries: LDS for the scores, global for the router
+    const float inv_beta = 1.0f / (float)s.beta;
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {
+        const int pr = tid + j * BA_THREADS;
+        if (pr < npairs) {
+            const int g = pr / H, i = pr - g * H;
+            const float kb0 = a0[j] * inv_beta, kb1 = a1[j] * inv_beta;
+            kb[g * D + i] = kb0;
+            kb[g * D + i + H] = kb1;
+            float *dst = kbar + (((size_t)b * Hkv + g) * s.NB + n) * D;
+            dst[i] = kb0;
+            dst[i + H] = kb1;
         }
     }
-    const float inv_beta = 1.0f / (float)beta;
-    const float kb0 = acc0 * inv_beta, kb1 = acc1 * inv_beta;
-    kb_s[wave][sub][i] = kb0;
-    kb_s[wave][sub][i + H] = kb1;
-    if (live) {
-        float *dst = kbar + (((size_t)b * s.Hkv + g) * s.NB + n) * D;
-        dst[i] = kb0;
-        dst[i + H] = kb1;
-    }
-    __builtin_amdgcn_wave_barrier();
     __syncthreads();
 
-    // Code scores: lane -> (task, component, code).
-    const int PK = s.P * s.K, ds = s.ds;
-    for (int ci = lane; ci < TPW * PK; ci += WAVE) {
-        const int ts = ci / PK, code = ci % PK, p = code / s.K;
-        const long task2 = ((long)blockIdx.x * 4 + wave) * TPW + ts;
-        if (task2 >= ntask) continue;
-        const int g2 = (int)(task2 % s.Hkv);
-        const float *crow = cb + ((size_t)g2 * PK + code) * ds;
-        const float *kv = &kb_s[wave][ts][p * ds];
+    // code scores: thread per (kv-head, component code); the code row is
+    // loaded whole before the chain starts
+    for (int x = tid; x < Hkv * PK; x += BA_THREADS) {
+        const int g = x / PK, code = x - g * PK, p = code / K;
+        const float4 *crow = reinterpret_cast<const float4 *>(cb + ((size_t)g * PK + code) * DS);
+        float4 cv[DS / 4];
+#pragma unroll
+        for (int j = 0; j < DS / 4; ++j) cv[j] = crow[j];
+        const float *kv = kb + g * D + p * DS;
         float acc = 0.0f;
-        for (int j = 0; j < ds; j += 4) {
-            const float4 cv = *reinterpret_cast<const float4 *>(crow + j);
-            acc = __builtin_fmaf(kv[j], cv.x, acc);
-            acc = __builtin_fmaf(kv[j + 1], cv.y, acc);
-            acc = __builtin_fmaf(kv[j + 2], cv.z, acc);
-            acc = __builtin_fmaf(kv[j + 3], cv.w, acc);
+#pragma unroll
+        for (int j = 0; j < DS / 4; ++j) {
+            acc = __builtin_fmaf(kv[4 * j], cv[j].x, acc);
+            acc = __builtin_fmaf(kv[4 * j + 1], cv[j].y, acc);
+            acc = __builtin_fmaf(kv[4 * j + 2], cv[j].z, acc);
+            acc = __builtin_fmaf(kv[4 * j + 3], cv[j].w, acc);
         }
-        sc_s[wave][ts][code] = acc;
+        sc[x] = acc;
     }
     __syncthreads();
-    // Per-component argmax, lowest code on ties.
-    if (lane < TPW * s.P) {
-        const int ts = lane / s.P, p = lane % s.P;
-        const float *sv = &sc_s[wave][ts][p * s.K];
-        int best = 0;
-        float bv = sv[0];
-        for (int c = 1; c < s.K; ++c)
-            if (sv[c] > bv) { bv = sv[c]; best = c; }
-        code_s[wave][ts][p] = best;
-    }
-    __syncthreads();
-    if (lane < TPW) {
-        const long task3 = ((long)blockIdx.x * 4 + wave) * TPW + lane;
-        if (task3 < ntask) {
-            const int g3 = (int)(task3 % s.Hkv);
-            const int n3 = (int)((task3 / s.Hkv) % s.NB);
-            const int b3 = (int)(task3 / ((long)s.Hkv * s.NB));
-            int a = 0;
-            for (int p = 0; p < s.P; ++p) a = a * s.K + code_s[wave][lane][p];
-            addr[((size_t)b3 * s.Hkv + g3) * s.NB + n3] = a;
+
+    // argmax per component (lowest code on ties), address = mixed radix
+    for (int g = tid; g < Hkv; g += BA_THREADS) {
+        int a = 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const float *sv = sc + g * PK + p * K;
+            int best = 0;
+            float bv = sv[0];
+#pragma unroll 8
+            for (int c = 1; c < K; ++c) {
+                const float v = sv[c];
+                best = v > bv ? c : best;
+                bv = v > bv ? v : bv;
+            }
+            a = a * K + best;
         }
+        addr[((size_t)b * Hkv + g) * s.NB + n] = a;
     }
 }
 
@@ -135,8 +217,8 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s,
     int32_t *hist = lds;            // [A] loads
     int32_t *off = lds + A;         // [A+1] list starts
     int32_t *run = lds + 2 * A + 1; // [A] blocks already placed per address
-    __shared__ int32_t part[PL_THREADS];
-    __shared__ int32_t ovf_s[PL_THREADS];
+    __shared__ int32_t part[PL_THREADS / WAVE];
+    __shared__ int32_t ovf_s[PL_THREADS / WAVE];
 
     const int u = blockIdx.x;  // b * Hkv + g
     const int32_t *ad = addr + (size_t)u * NB;
@@ -155,23 +237,35 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s,
         sum += min(l, cap);
         ov += max(0, l - cap);
     }
-    part[tid] = sum;
-    ovf_s[tid] = ov;
-    __syncthreads();
-    if (tid == 0) {
-        int acc = 0, o = 0;
-        for (int x = 0; x < PL_THREADS; ++x) {
-            const int v = part[x];
-            part[x] = acc;
-            acc += v;
-            o += ovf_s[x];
-        }
-        off[A] = acc;
-        overflow[u] = o;
+    // block-wide exclusive scan of the per-thread sums: wave prefix by
+    // shuffles, then the four wave totals
+    const int lane = tid & (WAVE - 1), wv = tid / WAVE;
+    int incl = sum;
+#pragma unroll
+    for (int dlt = 1; dlt < WAVE; dlt <<= 1) {
+        const int o = __shfl_up(incl, dlt);
+        if (lane >= dlt) incl += o;
     }
+    int ovw = ov;
+#pragma unroll
+    for (int dlt = 32; dlt > 0; dlt >>= 1) ovw += __shfl_xor(ovw, dlt);
+    if (lane == WAVE - 1) part[wv] = incl;
+    if (lane == 0) ovf_s[wv] = ovw;
     __syncthreads();
+    int wbase = 0, total_all = 0, ovf_all = 0;
+#pragma unroll
+    for (int w = 0; w < PL_THREADS / WAVE; ++w) {
+        const int v = part[w];
+        wbase += w < wv ? v : 0;
+        total_all += v;
+        ovf_all += ovf_s[w];
+    }
+    if (tid == 0) {
+        off[A] = total_all;
+        overflow[u] = ovf_all;
+    }
     {
-        int acc = part[tid];
+        int acc = wbase + incl - sum;
         for (int a = lo; a < hi; ++a) {
             off[a] = acc;
             acc += min(hist[a], cap);
@@ -211,25 +305,47 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s,
     }
 }
 
+// ---------------------------------------------------------------- launchers
+template <int D, int P, bool BF16, int MAXP>
+hipError_t launch_ba_t(const Shape &s, int ct, size_t lds, const void *k, const float *cos_t,
+                       const float *sin_t, const float *cb, float *kbar, int32_t *addr,
+                       hipStream_t st) {
+    auto *fn = k_block_address<D, P, BF16, MAXP>;
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    fn<<<dim3((unsigned)s.NB, (unsigned)s.B), BA_THREADS, lds, st>>>(s, ct, k, cos_t, sin_t, cb,
+                                                                     kbar, addr);
+    return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_ba(const Shape &s, const void *k, const float *cos_t, const float *sin_t,
+                     const float *cb, float *kbar, int32_t *addr, hipStream_t st) {
+    const int ct = block_chunk_tokens(s);
+    const size_t lds = block_address_lds(s, ct);
+    const bool small = s.Hkv * (D / 2) <= 2 * BA_THREADS;
+    if (s.P == 1)
+        return small ? launch_ba_t<D, 1, BF16, 2>(s, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st)
+                     : launch_ba_t<D, 1, BF16, 8>(s, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st);
+    return small ? launch_ba_t<D, 2, BF16, 2>(s, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st)
+                 : launch_ba_t<D, 2, BF16, 8>(s, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st);
+}
+
 }  // namespace
 
-// ---------------------------------------------------------------- launchers
 hipError_t launch_block_address(const Shape &s, const void *k, const float *cos_t,
                                 const float *sin_t, const float *cb, float *kbar, int32_t *addr,
                                 hipStream_t st) {
-    const long ntask = (long)s.B * s.NB * s.Hkv;
-    const int tpw = WAVE / (s.d / 2);
-    const long nwaves = (ntask + tpw - 1) / tpw;
-    const dim3 grid((unsigned)((nwaves + 3) / 4));
     const bool bf = s.dtype == 1;
-    if (s.d == 64) {
-        if (bf) k_block_address<64, true><<<grid, 256, 0, st>>>(s, k, cos_t, sin_t, cb, kbar, addr);
-        else k_block_address<64, false><<<grid, 256, 0, st>>>(s, k, cos_t, sin_t, cb, kbar, addr);
-    } else {
-        if (bf) k_block_address<128, true><<<grid, 256, 0, st>>>(s, k, cos_t, sin_t, cb, kbar, addr);
-        else k_block_address<128, false><<<grid, 256, 0, st>>>(s, k, cos_t, sin_t, cb, kbar, addr);
-    }
-    return hipGetLastError();
+    if (s.d == 64)
+        return bf ? launch_ba<64, true>(s, k, cos_t, sin_t, cb, kbar, addr, st)
+                  : launch_ba<64, false>(s, k, cos_t, sin_t, cb, kbar, addr, st);
+    return bf ? launch_ba<128, true>(s, k, cos_t, sin_t, cb, kbar, addr, st)
+              : launch_ba<128, false>(s, k, cos_t, sin_t, cb, kbar, addr, st);
 }
 
 hipError_t launch_posting_lists(const Shape &s, const int32_t *addr, int32_t *offsets,

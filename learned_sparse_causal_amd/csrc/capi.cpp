@@ -54,6 +54,7 @@ mono_status make_shape(const mono_config *c, bool mixer, Shape &s) {
     if (c->n_probes > 16) return MONO_ERR_UNSUPPORTED;
     const int NB = c->seq_len / c->block_size;
     if (NB > 8192) return MONO_ERR_UNSUPPORTED;
+    if ((long)c->n_kv_heads * c->head_dim > 4096) return MONO_ERR_UNSUPPORTED;
     if (c->n_remote > 16 && NB - c->n_local > c->n_remote) return MONO_ERR_UNSUPPORTED;
     const double routes = (double)c->batch * c->n_q_heads * c->seq_len;
     if (routes * c->n_remote >= 2147483647.0) return MONO_ERR_UNSUPPORTED;
