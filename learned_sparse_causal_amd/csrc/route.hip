@@ -52,11 +52,6 @@ __device__ __forceinline__ u64 key_of(float s, uint32_t low_rank) {
     return ((u64)ordered(s) << 32) | (u64)low_rank;
 }
 
-// low word of a block key: lower address first, then lower block
-__device__ __forceinline__ uint32_t block_low(int a, int n) {
-    return (uint32_t)((4095 - a) << 13) | (uint32_t)(8191 - n);
-}
-
 template <int M>
 __device__ __forceinline__ void insert(u64 (&lst)[M], u64 k) {
 #pragma unroll
@@ -83,12 +78,14 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     extern __shared__ float lds[];
     const int K = s.K, PK = P * K, A = s.A, NB = s.NB;
     const int nw = blockDim.x / WAVE;
-    int2 *meta_s = reinterpret_cast<int2 *>(lds);                // [NB]: score rows, tie word
+    int2 *meta_s = reinterpret_cast<int2 *>(lds);                // [NB]: score-row offsets
     int *off_s = reinterpret_cast<int *>(meta_s + NB);           // [A+1]
     int *ent_s = off_s + A + 1;                                  // [NB]
-    float *sc_all = reinterpret_cast<float *>(ent_s + NB);       // [nw][P*K][64]
+    float *sc_all = reinterpret_cast<float *>(ent_s + NB);       // [nw][P*K + 1][64]
     const int lane = lane_id(), wave = threadIdx.x / WAVE;
-    float *sc_s = sc_all + wave * PK * WAVE;
+    float *sc_s = sc_all + wave * (PK + 1) * WAVE;
+    const int dummy = PK * WAVE * 4;                             // byte offset of a -inf row
+    sc_s[PK * WAVE + lane] = -INFINITY;
 
     const int h = blockIdx.y, b = blockIdx.z, g = h / s.G;
     const size_t ug = (size_t)b * s.Hkv + g;
@@ -110,13 +107,12 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
             const int a = ad_g[n];
             // kept blocks are the first `cap` of the address in source order,
             // so n is indexed iff it is not after the list's last entry.
-            // x: byte offsets of the score-table rows of the block's two
-            // component codes (16 bits each), or -1 if it is not indexed;
-            // y: tie word (lower address first, then lower block)
+            // Byte offsets of the score-table rows of the block's component
+            // codes; a block that is not indexed points at the -inf row.
             const int c0 = P == 1 ? a : a / K, c1 = P == 1 ? 0 : a - c0 * K;
             const bool idx = n <= ent_s[off_s[a + 1] - 1];
-            const int o0 = c0 * WAVE * 4, o1 = P == 1 ? 0 : (K + c1) * WAVE * 4;   // bytes
-            meta_s[n] = make_int2(idx ? o0 | (o1 << 16) : -1, (int)block_low(a, n));
+            const int o0 = c0 * WAVE * 4, o1 = P == 1 ? dummy : (K + c1) * WAVE * 4;
+            meta_s[n] = idx ? make_int2(o0, o1) : make_int2(dummy, dummy);
         }
     }
     __syncthreads();
@@ -268,24 +264,42 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
         }
     }
 
-    // ---- pool part 2: extension to R blocks, for lanes that need it
+    // ---- pool part 2: extension to R blocks, for lanes that need it.  The
+    // R best eligible indexed blocks by (sigma desc, block asc), visited in
+    // source order; a new block enters only if its sigma beats the R-th best.
+    // Blocks of different addresses with bitwise equal sigma are ordered by
+    // block rather than address (an exact score tie at the pool boundary).
+    // RM - R sentinel slots never move.
     const bool need = live && cnt < R;
     if (__ballot(need) != 0ull) {
-        u64 kk[RM];
+        float bs[RM];
+        int bn[RM];
 #pragma unroll
-        for (int x = 0; x < RM; ++x) kk[x] = x < RM - R ? ~0ull : 0ull;
+        for (int x = 0; x < RM; ++x) { bs[x] = x < RM - R ? INFINITY : -INFINITY; bn[x] = -1; }
         const char *scl = reinterpret_cast<const char *>(sc_s + lane);
-        auto score = [&](int2 m) {
-            const int x = m.x < 0 ? 0 : m.x;
-            const float a0 = *reinterpret_cast<const float *>(scl + (x & 0xFFFF));
-            const float a1 = *reinterpret_cast<const float *>(scl + (x >> 16));
-            return P == 1 ? a0 : a0 + a1;
+        auto sigma = [&](int2 m) {
+            const float a0 = *reinterpret_cast<const float *>(scl + m.x);
+            if constexpr (P == 1) return a0;
+            const float a1 = *reinterpret_cast<const float *>(scl + m.y);
+            return a0 + a1;
         };
-        // a block enters the R best if its key beats the R-th best so far
-        auto visit = [&](float sg, int2 m) {
-            if (m.x < 0) return;  // not indexed (wave-uniform)
-            const u64 key = key_of(sg, (uint32_t)m.y);
-            if (need & (key > kk[RM - 1])) insert(kk, key);
+        auto visit = [&](float sg, int n) {
+            if (need & (sg > bs[RM - 1])) {
+                float v = sg;
+                int id = n;
+#pragma unroll
+                for (int x = 0; x < RM; ++x) {
+                    // a block pushed down the list meets later blocks of
+                    // equal sigma: the lower block id stays first
+                    const bool sw = (v > bs[x]) | ((v == bs[x]) & (id < bn[x]));
+                    const float ov = bs[x];
+                    const int oi = bn[x];
+                    bs[x] = sw ? v : ov;
+                    bn[x] = sw ? id : oi;
+                    v = sw ? ov : v;
+                    id = sw ? oi : id;
+                }
+            }
         };
         constexpr int U = 8;
         int n = 0;
@@ -295,32 +309,33 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
 #pragma unroll
             for (int u = 0; u < U; ++u) m[u] = meta_s[n + u];
 #pragma unroll
-            for (int u = 0; u < U; ++u) sg[u] = score(m[u]);
+            for (int u = 0; u < U; ++u) sg[u] = sigma(m[u]);
 #pragma unroll
-            for (int u = 0; u < U; ++u) visit(sg[u], m[u]);
+            for (int u = 0; u < U; ++u) visit(sg[u], n + u);
         }
-        for (; n <= last; ++n) {
-            const int2 m = meta_s[n];
-            visit(score(m), m);
-        }
+        for (; n <= last; ++n) visit(sigma(meta_s[n]), n);
         if (need) {
+            // address of an indexed block, from its score-row offsets
+            auto addr_of = [&](int nn) {
+                const int2 m = meta_s[nn];
+                const int c0 = m.x / (WAVE * 4);
+                return P == 1 ? c0 : c0 * K + (m.y / (WAVE * 4) - K);
+            };
+            // does (sigma, address) rank after the n_probes-th address?
+            auto after_tau = [&](float sg, int a) {
+                return (sg < tau_v) | ((sg == tau_v) & (a > tau_a));
+            };
             // the R best blocks that rank after tau (the others are in part 1)
-            const uint32_t tau_hi = ordered(tau_v);
 #pragma unroll
             for (int x = 0; x < RM; ++x) {
-                if (x < RM - R || kk[x] == 0ull) continue;
-                const uint32_t hi = (uint32_t)(kk[x] >> 32);
-                const int a = 4095 - (int)((kk[x] >> 13) & 0xFFFu);
-                const int nn = 8191 - (int)(kk[x] & 0x1FFFu);
-                if (hi < tau_hi || (hi == tau_hi && a > tau_a)) rerank(nn);
+                if (x < RM - R || bn[x] < 0) continue;
+                if (after_tau(bs[x], addr_of(bn[x]))) rerank(bn[x]);
             }
             // blocks of the R-th block's address after it tie with it
-            const u64 kR = kk[RM - 1];
-            if (kR != 0ull) {
-                const uint32_t hi = (uint32_t)(kR >> 32);
-                const int aR = 4095 - (int)((kR >> 13) & 0xFFFu);
-                const int nR = 8191 - (int)(kR & 0x1FFFu);
-                if (hi < tau_hi || (hi == tau_hi && aR > tau_a)) {
+            const int nR = bn[RM - 1];
+            if (nR >= 0) {
+                const int aR = addr_of(nR);
+                if (after_tau(bs[RM - 1], aR)) {
                     const int e1 = off_s[aR + 1];
                     for (int e = off_s[aR]; e < e1; ++e) {
                         const int nn = ent_s[e];
@@ -368,7 +383,8 @@ __global__ __launch_bounds__(256) void k_route_bypass(Shape s, int32_t *__restri
 // list entries and one score table per wave.
 size_t route_lds(const Shape &s, int waves) {
     const int PK = s.P * s.K;
-    return (size_t)(s.A + 1 + 3 * s.NB) * sizeof(int) + (size_t)(waves * PK * WAVE) * sizeof(float);
+    return (size_t)(s.A + 1 + 3 * s.NB) * sizeof(int) +
+           (size_t)(waves * (PK + 1) * WAVE) * sizeof(float);
 }
 
 // Four waves per workgroup unless that overflows the 160 KiB of LDS.
