@@ -66,6 +66,22 @@ __device__ __forceinline__ void load4(const void *base, size_t i, float *o) {
     }
 }
 
+// 4 elements held as raw 8-byte words (one for bf16, two for fp32) -> floats
+template <bool BF16>
+__device__ __forceinline__ void unpack4(const uint2 *w, float *o) {
+    if constexpr (BF16) {
+        o[0] = __uint_as_float(w[0].x << 16);
+        o[1] = __uint_as_float(w[0].x & 0xFFFF0000u);
+        o[2] = __uint_as_float(w[0].y << 16);
+        o[3] = __uint_as_float(w[0].y & 0xFFFF0000u);
+    } else {
+        o[0] = __uint_as_float(w[0].x);
+        o[1] = __uint_as_float(w[0].y);
+        o[2] = __uint_as_float(w[1].x);
+        o[3] = __uint_as_float(w[1].y);
+    }
+}
+
 __device__ __forceinline__ void store4(u16 *p, const float *x) {
     uint2 w;
     w.x = pack_bf16x2(x[0], x[1]);
@@ -439,16 +455,22 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
                                                       const int32_t *__restrict__ chunk_local,
                                                       const int32_t *__restrict__ wg_base,
                                                       const int32_t *__restrict__ seg_rel,
-                                                      int32_t *__restrict__ list,
                                                       int32_t *__restrict__ list_q,
-                                                      int32_t *__restrict__ chunk_bin) {
+                                                      int4 *__restrict__ chunk_desc) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < nbins) {
+        // descriptors {bin, first row, end row} of the bin's chunks
         const long nb = (long)nbins;
+        const int nwg = (int)((nb + BIN_WG - 1) / BIN_WG);
         const int c0 = wg_base[2 * (i / BIN_WG) + 1] + chunk_local[i];
         const int c1 = i + 1 < nb ? wg_base[2 * ((i + 1) / BIN_WG) + 1] + chunk_local[i + 1]
-                                  : wg_base[2 * ((nb + BIN_WG - 1) / BIN_WG) + 1];
-        for (int c = c0; c < c1; ++c) chunk_bin[c] = (int32_t)i;
+                                  : wg_base[2 * nwg + 1];
+        const int b0 = bin_start_of(bin_local, wg_base, i);
+        const int b1 = i + 1 < nb ? bin_start_of(bin_local, wg_base, i + 1) : wg_base[2 * nwg];
+        for (int c = c0; c < c1; ++c) {
+            const int r0 = b0 + (c - c0) * CHUNK_ROWS;
+            chunk_desc[c] = make_int4((int)i, r0, min(r0 + CHUNK_ROWS, b1), 0);
+        }
     }
     const long n = (long)s.B * s.Hq * s.T * s.R;
     if (i >= n) return;
@@ -463,17 +485,19 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
     entry_pos[i] = at;                                         // where its partial will be
 }
 
+// Persistent over a contiguous range of chunks.  Every wave walks its tasks
+// (16-row groups: group `wave`, `wave` + 4, ... of each chunk, possibly an
+// idle one) as one sequence across chunk boundaries: the list entry of the
+// task after next and the query rows of the next task are in flight while a
+// task computes.  The next chunk's K / V^T (if its bin differs) is staged in
+// registers during the current chunk and written to LDS after it.
 template <int D, int BETA, bool BF16>
 __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
                                                      const Elem<BF16> *__restrict__ k_rot,
                                                      const Elem<BF16> *__restrict__ v,
-                                                     const int32_t *__restrict__ list,
                                                      const int32_t *__restrict__ list_q,
-                                                     const int32_t *__restrict__ bin_local,
-                                                     const int32_t *__restrict__ chunk_local,
-                                                     const int32_t *__restrict__ wg_base,
-                                                     const int32_t *__restrict__ chunk_bin,
-                                                     int nbins,
+                                                     const int4 *__restrict__ chunk_desc,
+                                                     const int32_t *__restrict__ nchunks_p,
                                                      float *__restrict__ part_lse,
                                                      Elem<BF16> *__restrict__ part_o) {
     using T = Tile<D, BF16>;
@@ -483,84 +507,108 @@ __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *
     E *Ks = reinterpret_cast<E *>(smem);               // NSUB x [64][QS]
     E *Vts = Ks + NSUB * T::K_ELEMS;                    // NSUB x [D][VS]
 
-    const int nwg = (nbins + BIN_WG - 1) / BIN_WG;
-    const int nchunks = wg_base[2 * nwg + 1];
+    const int nchunks = *nchunks_p;
     const int per = (nchunks + gridDim.x - 1) / gridDim.x;
     const int c_beg = blockIdx.x * per, c_end = min(nchunks, c_beg + per);
-    const int T_ = s.T, Hkv = s.Hkv;
+    if (c_beg >= c_end) return;
+    const int T_ = s.T, Hkv = s.Hkv, NB = s.NB;
     const int lane = lane_id(), wave = threadIdx.x / WAVE, lr = lane & 15, lg = lane >> 4;
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
-    int loaded_bin = -1;
-    for (int chunk = c_beg; chunk < c_end; ++chunk) {
-        const int bin = chunk_bin[chunk];
-        const int bstart = bin_start_of(bin_local, wg_base, bin);
-        const int bend = bin + 1 < nbins ? bin_start_of(bin_local, wg_base, bin + 1) : wg_base[2 * nwg];
-        const int cstart = wg_base[2 * (bin / BIN_WG) + 1] + chunk_local[bin];
-        const int r0 = bstart + (chunk - cstart) * CHUNK_ROWS;
-        const int r1 = min(r0 + CHUNK_ROWS, bend);
-        const int n = bin % s.NB, g = (bin / s.NB) % s.Hkv, b = bin / (s.NB * s.Hkv);
 
-        // a row's entry id and q row, or -1 past the chunk
-        auto entry_of = [&](int grp) {
-            const int row = r0 + grp * 16 + lr;
-            return row < r1 ? make_int2(row, list_q[row]) : make_int2(-1, 0);
-        };
-        const int ngrp = (r1 - r0 + 15) / 16;
-        int grp = wave;
-        int2 e_cur = grp < ngrp ? entry_of(grp) : make_int2(-1, 0);
-        QFrags<D, BF16> qcur;
-        qcur.issue(q_rot, (size_t)e_cur.y * D, e_cur.x >= 0);
-
-        if (bin != loaded_bin) {   // consecutive chunks of one bin keep K/V in LDS
-            RowStager<D, BF16> ks[NSUB];
-            VtStager<D, BF16> vs[NSUB];
+    auto desc_at = [&](int c) { return c < c_end ? chunk_desc[c] : make_int4(-1, 0, 0, 0); };
+    auto ngroups = [&](const int4 &d) { return d.x < 0 ? 0 : (d.z - d.y + 15) / 16; };
+    // this lane's row of group grp of a chunk, or -1
+    auto row_of = [&](const int4 &d, int grp) {
+        const int row = d.y + grp * 16 + lr;
+        return (d.x >= 0 && row < d.z) ? row : -1;
+    };
+    RowStager<D, BF16> ks[NSUB];
+    VtStager<D, BF16> vs[NSUB];
+    auto kv_issue = [&](int bin) {
+        const int n = bin % NB, g = (bin / NB) % Hkv, b = bin / (NB * Hkv);
 #pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub) {
-                const int tb = n * BETA + sub * 64;
-                ks[sub].issue(k_rot, [&](int r, size_t &off) {
-                    off = (((size_t)b * T_ + tb + r) * Hkv + g) * D;
-                    return true;
-                });
-                vs[sub].issue(v, (((size_t)b * T_ + tb) * Hkv + g) * D, (size_t)Hkv * D);
-            }
-            __syncthreads();   // the previous chunk is done with Ks / Vts
-#pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub) {
-                ks[sub].commit(Ks + sub * T::K_ELEMS);
-                vs[sub].commit(Vts + sub * T::V_ELEMS);
-            }
-            __syncthreads();
-            loaded_bin = bin;
+        for (int sub = 0; sub < NSUB; ++sub) {
+            const int tb = n * BETA + sub * 64;
+            ks[sub].issue(k_rot, [&](int r, size_t &off) {
+                off = (((size_t)b * T_ + tb + r) * Hkv + g) * D;
+                return true;
+            });
+            vs[sub].issue(v, (((size_t)b * T_ + tb) * Hkv + g) * D, (size_t)Hkv * D);
         }
+    };
+    auto kv_commit = [&]() {
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+            ks[sub].commit(Ks + sub * T::K_ELEMS);
+            vs[sub].commit(Vts + sub * T::V_ELEMS);
+        }
+    };
 
-        int2 e_next = grp + 4 < ngrp ? entry_of(grp + 4) : make_int2(-1, 0);
-        for (; grp < ngrp; grp += 4) {
+    int4 dcur = desc_at(c_beg), dnext = desc_at(c_beg + 1), dnn = desc_at(c_beg + 2);
+    // task pipeline: Q of the current task, list entry of the next one
+    int row_cur = row_of(dcur, wave);
+    QFrags<D, BF16> qcur;
+    qcur.issue(q_rot, row_cur >= 0 ? (size_t)list_q[row_cur] * D : 0, row_cur >= 0);
+    int row_nx;
+    {
+        const bool same = wave + 4 < ngroups(dcur);
+        row_nx = same ? row_of(dcur, wave + 4) : row_of(dnext, wave);
+    }
+    int q_nx = row_nx >= 0 ? list_q[row_nx] : 0;
+    kv_issue(dcur.x);
+    kv_commit();
+    __syncthreads();
+
+    for (int c = c_beg; c < c_end; ++c) {
+        const bool stage = dnext.x >= 0 && dnext.x != dcur.x;
+        if (stage) kv_issue(dnext.x);   // in flight during this chunk
+        const int ng = ngroups(dcur), ng1 = ngroups(dnext);
+        for (int grp = wave;; grp += 4) {
             Frag8<BF16> qf[D / 32];
             qcur.get(qf);
-            // next group's Q in flight during this group's compute
-            const int e_now = e_cur.x;
-            if (grp + 4 < ngrp) qcur.issue(q_rot, (size_t)e_next.y * D, e_next.x >= 0);
-            e_cur = e_next;
-            e_next = grp + 8 < ngrp ? entry_of(grp + 8) : make_int2(-1, 0);
-            f32x4 o[D / 16];
+            const int row_now = row_cur;
+            // next task: grp + 4 of this chunk, else group `wave` of the next
+            const bool in_chunk = grp + 4 < ng;
+            const int row1 = row_nx;
+            if (row1 >= 0) qcur.issue(q_rot, (size_t)q_nx * D, true);
+            // the task after next
+            int row2;
+            if (in_chunk) row2 = grp + 8 < ng ? row_of(dcur, grp + 8) : row_of(dnext, wave);
+            else row2 = wave + 4 < ng1 ? row_of(dnext, wave + 4) : row_of(dnn, wave);
+            const int q2 = row2 >= 0 ? list_q[row2] : 0;
+            if (grp < ng) {   // wave-uniform: the group exists
+                f32x4 o[D / 16];
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            float m = -INFINITY, l = 0.0f;
+                for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                float m = -INFINITY, l = 0.0f;
 #pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub)
-                attend64<D, BF16>(qf, Ks + sub * T::K_ELEMS, Vts + sub * T::V_ELEMS, sl2, 0,
-                                  0x7fffffff, o, m, l);
-            if (e_now >= 0) {
-                if (lg == 0) part_lse[e_now] = m + __builtin_amdgcn_logf(l);
-                const float inv = 1.0f / l;
+                for (int sub = 0; sub < NSUB; ++sub)
+                    attend64<D, BF16>(qf, Ks + sub * T::K_ELEMS, Vts + sub * T::V_ELEMS, sl2, 0,
+                                      0x7fffffff, o, m, l);
+                if (row_now >= 0) {
+                    if (lg == 0) part_lse[row_now] = m + __builtin_amdgcn_logf(l);
+                    const float inv = 1.0f / l;
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) {
-                    const float x[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv,
-                                        o[dt][3] * inv};
-                    store4(part_o + (size_t)e_now * D + dt * 16 + 4 * lg, x);
+                    for (int dt = 0; dt < D / 16; ++dt) {
+                        const float x[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv,
+                                            o[dt][3] * inv};
+                        store4(part_o + (size_t)row_now * D + dt * 16 + 4 * lg, x);
+                    }
                 }
             }
+            row_cur = row1;
+            row_nx = row2;
+            q_nx = q2;
+            if (!in_chunk) break;
         }
+        __syncthreads();   // every wave is done with this chunk's K / V^T
+        if (stage) {
+            kv_commit();
+            __syncthreads();
+        }
+        dcur = dnext;
+        dnext = dnn;
+        dnn = desc_at(c + 3);
     }
 }
 
@@ -583,10 +631,14 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
 
     const int ntt = s.T / 64;
     // each workgroup walks a contiguous run of items: the tiles of one
-    // (batch, head), latest first, so adjacent tiles share K/V in its L2
+    // (batch, head), latest first.  A tile's local blocks are attended latest
+    // first, so the last key sub-tile of one tile is usually the first of the
+    // next one; it stays in LDS (resident_bh / resident_kb) and is not loaded
+    // again.
     const int nitems = s.B * s.Hq * ntt;
     const int per = (nitems + gridDim.x - 1) / gridDim.x;
     const int i_end = min(nitems, (int)blockIdx.x * per + per);
+    int resident_bh = -1, resident_kb = -1;
     for (int item = blockIdx.x * per; item < i_end; ++item) {
     __syncthreads();   // the previous item is done with LDS
     const int tt = ntt - 1 - item % ntt;
@@ -611,6 +663,20 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     for (int r = 0; r < RP; ++r) ep_pre[r] = (!uni && r < R) ? entry_pos[route * R + r] : -1;
 #pragma unroll
     for (int r = 0; r < RP; ++r) lse_pre[r] = ep_pre[r] >= 0 ? part_lse[ep_pre[r]] : 0.0f;
+    // the partial outputs of the first RPO slots, in flight from the start
+    constexpr int RPO = 2;
+    constexpr int NQ = BF16 ? 1 : 2;          // 8-byte words per 4 elements
+    uint2 o_pre[RPO][D / 16][NQ];
+#pragma unroll
+    for (int r = 0; r < RPO; ++r)
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+            for (int w = 0; w < NQ; ++w)
+                o_pre[r][dt][w] = ep_pre[r] >= 0
+                    ? reinterpret_cast<const uint2 *>(part_o + (size_t)ep_pre[r] * D + dt * 16 +
+                                                      4 * lg)[w]
+                    : make_uint2(0u, 0u);
     if (uni) {  // shared remote blocks of the tile: valid first occurrences of row 0
         const int32_t *row0 = sel + route0 * R;
         for (int r = threadIdx.x; r < R; r += blockDim.x) {
@@ -628,14 +694,17 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.0f;
 
-    // work items: (block, 64-key sub-tile) in order, skipping sub-tiles after the tile
+    // work items: (block, 64-key sub-tile): the local blocks latest first
+    // (sub-tiles latest first), then the shared remote blocks; sub-tiles after
+    // the tile's last query are skipped
     const int nrem = uni ? R : 0;
     const int lo_blk = max(0, qb - L + 1);
-    const int nblk = nrem + (qb - lo_blk + 1);
+    const int nloc = qb - lo_blk + 1;
+    const int nblk = nloc + nrem;
     auto item_key0 = [&](int j, int sub) {   // first key of item, or -1 if absent
-        const int blk = j < nrem ? blk_s[j] : lo_blk + (j - nrem);
+        const int blk = j < nloc ? qb - j : blk_s[j - nloc];
         if (blk < 0) return -1;
-        const int kb0 = blk * BETA + sub * 64;
+        const int kb0 = blk * BETA + (j < nloc ? BETA / 64 - 1 - sub : sub) * 64;
         return kb0 > t0 + 63 ? -1 : kb0;
     };
     auto next_item = [&](int &j, int &sub) {   // advance to the next present item
@@ -656,12 +725,17 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
         vst.issue(v, (((size_t)b * T_ + kb0) * Hkv + g) * D, (size_t)Hkv * D);
     };
     int kb_cur = j < nblk ? item_key0(j, sub) : -1;
-    if (kb_cur >= 0) issue_kv(kb_cur);
+    const bool reuse = kb_cur >= 0 && bh == resident_bh && kb_cur == resident_kb;
+    if (kb_cur >= 0 && !reuse) issue_kv(kb_cur);
     Frag8<BF16> qf[D / 32];
     qst.get(qf);
-    if (kb_cur >= 0) {
+    if (kb_cur >= 0 && !reuse) {
         kst.commit(Ks);
         vst.commit(Vt);
+    }
+    if (kb_cur >= 0) {
+        resident_bh = bh;
+        resident_kb = kb_cur;
     }
     __syncthreads();
     while (kb_cur >= 0) {
@@ -675,6 +749,10 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
             kst.commit(Ks);
             vst.commit(Vt);
             __syncthreads();
+        }
+        if (kb_next >= 0) {
+            resident_bh = bh;
+            resident_kb = kb_next;
         }
         j = jn;
         sub = sn;
@@ -701,7 +779,20 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
         for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[dt][r] *= wsum;
-        for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int r = 0; r < RPO; ++r) {   // prefetched slots (static indexes)
+            if (r >= R || ep_pre[r] < 0) continue;
+            const float w = __builtin_amdgcn_exp2f(lse_pre[r] - M);
+            wsum += w;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                float x[4];
+                unpack4<BF16>(o_pre[r][dt], x);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[rr];
+            }
+        }
+        for (int r = RPO; r < R; ++r) {
             if (ep_at(r) < 0) continue;
             const long e = ep_at(r);
             const float w = __builtin_amdgcn_exp2f(lse_at(r) - M);
@@ -748,8 +839,8 @@ unsigned persistent_grid(F *fn, size_t lds, long items) {
 }
 
 struct AttnWs {
-    int32_t *cnt, *seg_rel, *bin_local, *chunk_local, *wg_sum, *chunk_bin, *tile_flag,
-        *entry_pos, *list, *list_q;
+    int32_t *cnt, *seg_rel, *bin_local, *chunk_local, *wg_sum, *tile_flag, *entry_pos, *list_q;
+    int4 *chunk_desc;
     float *part_lse;
     void *part_o, *q_rot, *k_rot;
 };
@@ -786,8 +877,8 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     k_attn_scan<<<1, 1024, 0, st>>>(nwg, w.wg_sum);
     const long nscat = std::max<long>(nent, nbins);
     k_attn_scatter<<<dim3((unsigned)((nscat + 255) / 256)), 256, 0, st>>>(
-        s, nseg, nbins, sel, w.entry_pos, w.bin_local, w.chunk_local, w.wg_sum, w.seg_rel, w.list,
-        w.list_q, w.chunk_bin);
+        s, nseg, nbins, sel, w.entry_pos, w.bin_local, w.chunk_local, w.wg_sum, w.seg_rel,
+        w.list_q, w.chunk_desc);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const size_t lds_r = (size_t)((BETA / 64) * (T::K_ELEMS + T::V_ELEMS)) * sizeof(E);
@@ -796,9 +887,8 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     const unsigned grid_r = persistent_grid(k_attn_remote<D, BETA, BF16>, lds_r, max_chunks(s));
     k_attn_remote<D, BETA, BF16><<<dim3(grid_r), 256, lds_r, st>>>(
         s, reinterpret_cast<const E *>(w.q_rot), reinterpret_cast<const E *>(w.k_rot),
-        reinterpret_cast<const E *>(v), w.list, w.list_q, w.bin_local, w.chunk_local, w.wg_sum,
-        w.chunk_bin,
-        nbins, w.part_lse, reinterpret_cast<E *>(w.part_o));
+        reinterpret_cast<const E *>(v), w.list_q, w.chunk_desc, w.wg_sum + 2 * nwg + 1,
+        w.part_lse, reinterpret_cast<E *>(w.part_o));
     const size_t lds_l = (size_t)(T::K_ELEMS + T::V_ELEMS) * sizeof(E) +
                          (size_t)s.R * sizeof(int);
     err = ensure_lds(k_attn_local<D, BETA, BF16>, lds_l);
@@ -828,10 +918,10 @@ size_t attention_ws_layout(const Shape &s, size_t *off) {
     off[2] = p; p = al(p + nbins * 4);                        // bin start within workgroup
     off[3] = p; p = al(p + nbins * 4);                        // chunk start within workgroup
     off[4] = p; p = al(p + (2 * nwg + 2) * 4);                // workgroup bases and totals
-    off[5] = p; p = al(p + (size_t)max_chunks(s) * 4);        // chunk -> bin
+    off[5] = p; p = al(p + (size_t)max_chunks(s) * 16);       // chunk descriptors
     off[6] = p; p = al(p + ntiles * 4);                       // tile flags
     off[7] = p; p = al(p + nent * 4);                         // entry ranks
-    off[8] = p; p = al(p + nent * 4);                         // list
+    off[8] = p;                                               // (unused)
     off[9] = p; p = al(p + nent * 4);                         // partial lse
     off[10] = p; p = al(p + nent * (size_t)s.d * esz);        // partial outputs
     off[11] = p; p = al(p + (size_t)s.B * s.T * s.Hq * s.d * esz);   // rotated q
@@ -852,10 +942,9 @@ hipError_t launch_attention(const Shape &s, const void *q, const void *k, const 
     w.bin_local = reinterpret_cast<int32_t *>(base + off[2]);
     w.chunk_local = reinterpret_cast<int32_t *>(base + off[3]);
     w.wg_sum = reinterpret_cast<int32_t *>(base + off[4]);
-    w.chunk_bin = reinterpret_cast<int32_t *>(base + off[5]);
+    w.chunk_desc = reinterpret_cast<int4 *>(base + off[5]);
     w.tile_flag = reinterpret_cast<int32_t *>(base + off[6]);
     w.entry_pos = reinterpret_cast<int32_t *>(base + off[7]);
-    w.list = reinterpret_cast<int32_t *>(base + off[8]);
     w.part_lse = reinterpret_cast<float *>(base + off[9]);
     w.part_o = base + off[10];
     w.q_rot = base + off[11];
