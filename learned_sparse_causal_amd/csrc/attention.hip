@@ -199,11 +199,13 @@ struct QFrags {
 
 // One wave, 16 queries (B fragments of Q^T in registers: lane l holds row
 // l%16, dims 32c + 8(l/16) .. +7) against 64 keys, folded into the running
-// softmax state (m, l in log2 units, o unnormalized).  Keys with global index
-// > qlimit are masked (causality).
-template <int D, bool BF16>
+// softmax state (m, l in log2 units, o unnormalized).  The query rows are
+// pre-scaled by log2(e)/sqrt(d), so scores are base-2 logits.  MASK: keys
+// with global index > qlimit are masked (causality).  FIRST: the state is
+// empty on entry (m = -inf, l = 0, o = 0), so nothing is rescaled.
+template <int D, bool BF16, bool MASK, bool FIRST>
 __device__ __forceinline__ void attend64(const Frag8<BF16> (&qf)[D / 32], const Elem<BF16> *Ks,
-                                         const Elem<BF16> *Vt, float sl2, int key0, int qlimit,
+                                         const Elem<BF16> *Vt, int key0, int qlimit,
                                          f32x4 (&o)[D / 16], float &m, float &l) {
     using T = Tile<D, BF16>;
     const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
@@ -218,38 +220,45 @@ __device__ __forceinline__ void attend64(const Frag8<BF16> (&qf)[D / 32], const 
             mma32(st[mt], kf, qf[c]);
         }
     }
-    float mx = m;
+    float mx = FIRST ? -INFINITY : m;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int key = key0 + mt * 16 + 4 * lg + r;
-            const float z = key <= qlimit ? st[mt][r] * sl2 : -INFINITY;
-            st[mt][r] = z;
-            mx = fmaxf(mx, z);
+            if constexpr (MASK) {
+                const int key = key0 + mt * 16 + 4 * lg + r;
+                st[mt][r] = key <= qlimit ? st[mt][r] : -INFINITY;
+            }
+            mx = fmaxf(mx, st[mt][r]);
         }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool none = mx == -INFINITY;
-    const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m - mx);
+    // a row with every key masked so far keeps mx = -inf: no key contributes
+    const bool none = MASK && mx == -INFINITY;
+    const float msub = none ? 0.0f : mx;
     float p[4][4];
     float ps = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float z = st[mt][r];
-            p[mt][r] = (z == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z - mx);
+            p[mt][r] = __builtin_amdgcn_exp2f(st[mt][r] - msub);   // exp2(-inf) = 0
             ps += p[mt][r];
         }
     }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
-    l = l * alpha + ps;
-    if (!none) m = mx;
+    if constexpr (FIRST) {
+        l = ps;
+        m = mx;
+    } else {
+        const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m - mx);
+        l = l * alpha + ps;
+        if (!none) m = mx;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+        for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+    }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const float pv[8] = {p[2 * c][0], p[2 * c][1], p[2 * c][2], p[2 * c][3],
@@ -340,6 +349,8 @@ __global__ __launch_bounds__(256) void k_attn_rotate(Shape s, const void *__rest
             src = k;
             dst = k_rot;
         }
+        // query rows carry the softmax scale log2(e)/sqrt(d) (base-2 logits)
+        const float sc = hd < s.Hq ? 1.4426950408889634f / sqrtf((float)D) : 1.0f;
         float x0[4], x1[4], o0[4], o1[4];
         load4<BF16>(src, off + i, x0);
         load4<BF16>(src, off + i + H, x1);
@@ -350,8 +361,8 @@ __global__ __launch_bounds__(256) void k_attn_rotate(Shape s, const void *__rest
         for (int e = 0; e < 4; ++e) {
             const float p0 = x0[e] * cc[e], p1 = x1[e] * ss[e];
             const float p2 = x1[e] * cc[e], p3 = x0[e] * ss[e];
-            o0[e] = p0 - p1;
-            o1[e] = p2 + p3;
+            o0[e] = (p0 - p1) * sc;
+            o1[e] = (p2 + p3) * sc;
         }
         store4(dst + off + i, o0);
         store4(dst + off + i + H, o1);
@@ -491,13 +502,41 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
 // task after next and the query rows of the next task are in flight while a
 // task computes.  The next chunk's K / V^T (if its bin differs) is staged in
 // registers during the current chunk and written to LDS after it.
+// Work split of the remote kernel: chunk c costs its rows plus CHUNK_OVH (the
+// K/V load and synchronization it brings), so the cost before chunk c is
+// r0(c) + CHUNK_OVH * c.  Workgroup w of `grid` takes the chunks whose cost
+// prefix falls in [w, w + 1) * total / grid; wg_first[w] is its first chunk
+// and wg_first[grid] = nchunks.
+constexpr int CHUNK_OVH = 128;
+constexpr int MAX_REMOTE_GRID = 8192;   // bound of the remote kernel's persistent grid
+
+__global__ __launch_bounds__(256) void k_attn_split(int grid, const int4 *__restrict__ chunk_desc,
+                                                    const int32_t *__restrict__ totals,
+                                                    int32_t *__restrict__ wg_first) {
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    const int rows = totals[0], nchunks = totals[1];
+    if (c == 0 && nchunks == 0)
+        for (int w = 0; w <= grid; ++w) wg_first[w] = 0;
+    if (c >= nchunks) return;
+    const double total = (double)rows + (double)CHUNK_OVH * nchunks;
+    auto owner = [&](int cc) {
+        const double pre = (double)chunk_desc[cc].y + (double)CHUNK_OVH * cc;
+        return min(grid - 1, (int)(pre * grid / total));
+    };
+    const int o = owner(c);
+    const int op = c > 0 ? owner(c - 1) : -1;
+    for (int w = op + 1; w <= o; ++w) wg_first[w] = c;
+    if (c == nchunks - 1)
+        for (int w = o + 1; w <= grid; ++w) wg_first[w] = nchunks;
+}
+
 template <int D, int BETA, bool BF16>
 __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
                                                      const Elem<BF16> *__restrict__ k_rot,
                                                      const Elem<BF16> *__restrict__ v,
                                                      const int32_t *__restrict__ list_q,
                                                      const int4 *__restrict__ chunk_desc,
-                                                     const int32_t *__restrict__ nchunks_p,
+                                                     const int32_t *__restrict__ wg_first,
                                                      float *__restrict__ part_lse,
                                                      Elem<BF16> *__restrict__ part_o) {
     using T = Tile<D, BF16>;
@@ -507,14 +546,10 @@ __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *
     E *Ks = reinterpret_cast<E *>(smem);               // NSUB x [64][QS]
     E *Vts = Ks + NSUB * T::K_ELEMS;                    // NSUB x [D][VS]
 
-    const int nchunks = *nchunks_p;
-    const int per = (nchunks + gridDim.x - 1) / gridDim.x;
-    const int c_beg = blockIdx.x * per, c_end = min(nchunks, c_beg + per);
+    const int c_beg = wg_first[blockIdx.x], c_end = wg_first[blockIdx.x + 1];
     if (c_beg >= c_end) return;
     const int T_ = s.T, Hkv = s.Hkv, NB = s.NB;
     const int lane = lane_id(), wave = threadIdx.x / WAVE, lr = lane & 15, lg = lane >> 4;
-    const float sl2 = 1.4426950408889634f / sqrtf((float)D);
-
     auto desc_at = [&](int c) { return c < c_end ? chunk_desc[c] : make_int4(-1, 0, 0, 0); };
     auto ngroups = [&](const int4 &d) { return d.x < 0 ? 0 : (d.z - d.y + 15) / 16; };
     // this lane's row of group grp of a chunk, or -1
@@ -581,10 +616,10 @@ __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *
 #pragma unroll
                 for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 float m = -INFINITY, l = 0.0f;
-#pragma unroll
-                for (int sub = 0; sub < NSUB; ++sub)
-                    attend64<D, BF16>(qf, Ks + sub * T::K_ELEMS, Vts + sub * T::V_ELEMS, sl2, 0,
-                                      0x7fffffff, o, m, l);
+                attend64<D, BF16, false, true>(qf, Ks, Vts, 0, 0, o, m, l);
+                if constexpr (NSUB > 1)
+                    attend64<D, BF16, false, false>(qf, Ks + T::K_ELEMS, Vts + T::V_ELEMS, 0, 0, o,
+                                                    m, l);
                 if (row_now >= 0) {
                     if (lg == 0) part_lse[row_now] = m + __builtin_amdgcn_logf(l);
                     const float inv = 1.0f / l;
@@ -688,7 +723,6 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     }
     __syncthreads();
 
-    const float sl2 = 1.4426950408889634f / sqrtf((float)D);
     f32x4 o[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -743,7 +777,7 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
         next_item(jn, sn);
         const int kb_next = jn < nblk ? item_key0(jn, sn) : -1;
         if (kb_next >= 0) issue_kv(kb_next);   // in flight during this compute
-        attend64<D, BF16>(qf, Ks, Vt, sl2, kb_cur, tq, o, m, l);
+        attend64<D, BF16, true, false>(qf, Ks, Vt, kb_cur, tq, o, m, l);
         __syncthreads();
         if (kb_next >= 0) {
             kst.commit(Ks);
@@ -839,7 +873,8 @@ unsigned persistent_grid(F *fn, size_t lds, long items) {
 }
 
 struct AttnWs {
-    int32_t *cnt, *seg_rel, *bin_local, *chunk_local, *wg_sum, *tile_flag, *entry_pos, *list_q;
+    int32_t *cnt, *seg_rel, *bin_local, *chunk_local, *wg_sum, *tile_flag, *entry_pos, *list_q,
+        *wg_first;
     int4 *chunk_desc;
     float *part_lse;
     void *part_o, *q_rot, *k_rot;
@@ -884,11 +919,14 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     const size_t lds_r = (size_t)((BETA / 64) * (T::K_ELEMS + T::V_ELEMS)) * sizeof(E);
     err = ensure_lds(k_attn_remote<D, BETA, BF16>, lds_r);
     if (err != hipSuccess) return err;
-    const unsigned grid_r = persistent_grid(k_attn_remote<D, BETA, BF16>, lds_r, max_chunks(s));
+    const unsigned grid_r = std::min<unsigned>(
+        persistent_grid(k_attn_remote<D, BETA, BF16>, lds_r, max_chunks(s)), MAX_REMOTE_GRID);
+    k_attn_split<<<dim3((unsigned)((max_chunks(s) + 255) / 256)), 256, 0, st>>>(
+        (int)grid_r, w.chunk_desc, w.wg_sum + 2 * nwg, w.wg_first);
     k_attn_remote<D, BETA, BF16><<<dim3(grid_r), 256, lds_r, st>>>(
         s, reinterpret_cast<const E *>(w.q_rot), reinterpret_cast<const E *>(w.k_rot),
-        reinterpret_cast<const E *>(v), w.list_q, w.chunk_desc, w.wg_sum + 2 * nwg + 1,
-        w.part_lse, reinterpret_cast<E *>(w.part_o));
+        reinterpret_cast<const E *>(v), w.list_q, w.chunk_desc, w.wg_first, w.part_lse,
+        reinterpret_cast<E *>(w.part_o));
     const size_t lds_l = (size_t)(T::K_ELEMS + T::V_ELEMS) * sizeof(E) +
                          (size_t)s.R * sizeof(int);
     err = ensure_lds(k_attn_local<D, BETA, BF16>, lds_l);
@@ -921,7 +959,7 @@ size_t attention_ws_layout(const Shape &s, size_t *off) {
     off[5] = p; p = al(p + (size_t)max_chunks(s) * 16);       // chunk descriptors
     off[6] = p; p = al(p + ntiles * 4);                       // tile flags
     off[7] = p; p = al(p + nent * 4);                         // entry ranks
-    off[8] = p;                                               // (unused)
+    off[8] = p; p = al(p + (size_t)(MAX_REMOTE_GRID + 1) * 4);   // remote work split
     off[9] = p; p = al(p + nent * 4);                         // partial lse
     off[10] = p; p = al(p + nent * (size_t)s.d * esz);        // partial outputs
     off[11] = p; p = al(p + (size_t)s.B * s.T * s.Hq * s.d * esz);   // rotated q
@@ -950,6 +988,7 @@ hipError_t launch_attention(const Shape &s, const void *q, const void *k, const 
     w.q_rot = base + off[11];
     w.k_rot = base + off[12];
     w.list_q = reinterpret_cast<int32_t *>(base + off[13]);
+    w.wg_first = reinterpret_cast<int32_t *>(base + off[8]);
     const bool bf = s.dtype == 1;
 #define MONO_ATTN_ARGS s, q, k, v, cos_t, sin_t, sel, out, w, st
     if (s.d == 64) {
