@@ -66,21 +66,59 @@ __device__ __forceinline__ void load4(const void *base, size_t i, float *o) {
     }
 }
 
-// 4 elements held as raw 8-byte words (one for bf16, two for fp32) -> floats
-template <bool BF16>
-__device__ __forceinline__ void unpack4(const uint2 *w, float *o) {
-    if constexpr (BF16) {
-        o[0] = __uint_as_float(w[0].x << 16);
-        o[1] = __uint_as_float(w[0].x & 0xFFFF0000u);
-        o[2] = __uint_as_float(w[0].y << 16);
-        o[3] = __uint_as_float(w[0].y & 0xFFFF0000u);
-    } else {
-        o[0] = __uint_as_float(w[0].x);
-        o[1] = __uint_as_float(w[0].y);
-        o[2] = __uint_as_float(w[1].x);
-        o[3] = __uint_as_float(w[1].y);
+// Partial outputs are stored lane-chunked: the values a lane holds for one
+// row in the MFMA output layout (dims 16 dt + 4 lg + r, in (dt, r) order) go
+// out as NCH 16-byte chunks, chunk j at 16-byte slot 4 j + lg of the row, so
+// one store instruction writes 64 contiguous bytes of each of its 16 rows.
+template <int D, bool BF16>
+struct PartChunks {
+    static constexpr int NCH = D * (BF16 ? 2 : 4) / 64;
+    u32x4 c[NCH];
+    __device__ __forceinline__ void pack(const float (&v)[D / 16][4]) {
+        if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                c[j] = u32x4{pack_bf16x2(v[2 * j][0], v[2 * j][1]), pack_bf16x2(v[2 * j][2], v[2 * j][3]),
+                             pack_bf16x2(v[2 * j + 1][0], v[2 * j + 1][1]),
+                             pack_bf16x2(v[2 * j + 1][2], v[2 * j + 1][3])};
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                c[j] = u32x4{__float_as_uint(v[j][0]), __float_as_uint(v[j][1]),
+                             __float_as_uint(v[j][2]), __float_as_uint(v[j][3])};
+        }
     }
-}
+    __device__ __forceinline__ void unpack(float (&v)[D / 16][4]) const {
+        if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    v[2 * j + h][0] = __uint_as_float(c[j][2 * h] << 16);
+                    v[2 * j + h][1] = __uint_as_float(c[j][2 * h] & 0xFFFF0000u);
+                    v[2 * j + h][2] = __uint_as_float(c[j][2 * h + 1] << 16);
+                    v[2 * j + h][3] = __uint_as_float(c[j][2 * h + 1] & 0xFFFF0000u);
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[j][r] = __uint_as_float(c[j][r]);
+        }
+    }
+    __device__ __forceinline__ void store(Elem<BF16> *row, int lg) const {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) reinterpret_cast<u32x4 *>(row)[4 * j + lg] = c[j];
+    }
+    __device__ __forceinline__ void load(const Elem<BF16> *row, int lg) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) c[j] = reinterpret_cast<const u32x4 *>(row)[4 * j + lg];
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) c[j] = u32x4{0u, 0u, 0u, 0u};
+    }
+};
 
 __device__ __forceinline__ void store4(u16 *p, const float *x) {
     uint2 w;
@@ -623,12 +661,14 @@ __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *
                 if (row_now >= 0) {
                     if (lg == 0) part_lse[row_now] = m + __builtin_amdgcn_logf(l);
                     const float inv = 1.0f / l;
+                    float x[D / 16][4];
 #pragma unroll
-                    for (int dt = 0; dt < D / 16; ++dt) {
-                        const float x[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv,
-                                            o[dt][3] * inv};
-                        store4(part_o + (size_t)row_now * D + dt * 16 + 4 * lg, x);
-                    }
+                    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) x[dt][r] = o[dt][r] * inv;
+                    PartChunks<D, BF16> pc;
+                    pc.pack(x);
+                    pc.store(part_o + (size_t)row_now * D, lg);
                 }
             }
             row_cur = row1;
@@ -662,7 +702,8 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     extern __shared__ __align__(16) unsigned char smem[];
     E *Ks = reinterpret_cast<E *>(smem);
     E *Vt = Ks + T::K_ELEMS;
-    int *blk_s = reinterpret_cast<int *>(Vt + T::V_ELEMS);  // [R] shared remote blocks
+    E *Ostg = Vt + T::V_ELEMS;                               // 4 waves x [16][D + 16 B]
+    int *blk_s = reinterpret_cast<int *>(Ostg + 4 * 16 * (D + 16 / sizeof(E)));  // [R]
 
     const int ntt = s.T / 64;
     // each workgroup walks a contiguous run of items: the tiles of one
@@ -700,18 +741,12 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     for (int r = 0; r < RP; ++r) lse_pre[r] = ep_pre[r] >= 0 ? part_lse[ep_pre[r]] : 0.0f;
     // the partial outputs of the first RPO slots, in flight from the start
     constexpr int RPO = 2;
-    constexpr int NQ = BF16 ? 1 : 2;          // 8-byte words per 4 elements
-    uint2 o_pre[RPO][D / 16][NQ];
+    PartChunks<D, BF16> o_pre[RPO];
 #pragma unroll
-    for (int r = 0; r < RPO; ++r)
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-            for (int w = 0; w < NQ; ++w)
-                o_pre[r][dt][w] = ep_pre[r] >= 0
-                    ? reinterpret_cast<const uint2 *>(part_o + (size_t)ep_pre[r] * D + dt * 16 +
-                                                      4 * lg)[w]
-                    : make_uint2(0u, 0u);
+    for (int r = 0; r < RPO; ++r) {
+        if (ep_pre[r] >= 0) o_pre[r].load(part_o + (size_t)ep_pre[r] * D, lg);
+        else o_pre[r].zero();
+    }
     if (uni) {  // shared remote blocks of the tile: valid first occurrences of row 0
         const int32_t *row0 = sel + route0 * R;
         for (int r = threadIdx.x; r < R; r += blockDim.x) {
@@ -818,26 +853,26 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
             if (r >= R || ep_pre[r] < 0) continue;
             const float w = __builtin_amdgcn_exp2f(lse_pre[r] - M);
             wsum += w;
+            float x[D / 16][4];
+            o_pre[r].unpack(x);
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                float x[4];
-                unpack4<BF16>(o_pre[r][dt], x);
+            for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[rr];
-            }
+                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
         }
         for (int r = RPO; r < R; ++r) {
             if (ep_at(r) < 0) continue;
             const long e = ep_at(r);
             const float w = __builtin_amdgcn_exp2f(lse_at(r) - M);
             wsum += w;
+            PartChunks<D, BF16> pc;
+            pc.load(part_o + (size_t)e * D, lg);
+            float x[D / 16][4];
+            pc.unpack(x);
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                float x[4];
-                load4<BF16>(part_o, (size_t)e * D + dt * 16 + 4 * lg, x);
+            for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[rr];
-            }
+                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
         }
         const float iw = 1.0f / wsum;
 #pragma unroll
@@ -845,9 +880,26 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[dt][r] *= iw;
     }
-    E *op = out + (((size_t)b * T_ + tq) * Hq + h) * D;
+    // output rows through the wave's LDS staging area, so that each lane
+    // stores 16 contiguous bytes and a store instruction covers 64 bytes of
+    // each of the wave's 16 rows
+    {
+        constexpr int VE = 16 / sizeof(E);           // elements per 16 bytes
+        constexpr int OS = D + VE;                   // staging row stride (elements)
+        E *stg = Ostg + wave * 16 * OS;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) store4(op + dt * 16 + 4 * lg, acc[dt]);
+        for (int dt = 0; dt < D / 16; ++dt) store4(stg + lr * OS + dt * 16 + 4 * lg, acc[dt]);
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        const int rr = lane >> 2, qq = lane & 3;
+        E *orow = out + (((size_t)b * T_ + t0 + wave * 16 + rr) * Hq + h) * D;
+#pragma unroll
+        for (int j = 0; j < D / (4 * VE); ++j) {
+            const int d0 = j * 4 * VE + qq * VE;
+            *reinterpret_cast<u32x4 *>(orow + d0) =
+                *reinterpret_cast<const u32x4 *>(stg + rr * OS + d0);
+        }
+    }
     }
 }
 
@@ -927,8 +979,8 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
         s, reinterpret_cast<const E *>(w.q_rot), reinterpret_cast<const E *>(w.k_rot),
         reinterpret_cast<const E *>(v), w.list_q, w.chunk_desc, w.wg_first, w.part_lse,
         reinterpret_cast<E *>(w.part_o));
-    const size_t lds_l = (size_t)(T::K_ELEMS + T::V_ELEMS) * sizeof(E) +
-                         (size_t)s.R * sizeof(int);
+    const size_t lds_l = (size_t)(T::K_ELEMS + T::V_ELEMS + 4 * 16 * (D + 16 / sizeof(E))) *
+                             sizeof(E) + (size_t)s.R * sizeof(int);
     err = ensure_lds(k_attn_local<D, BETA, BF16>, lds_l);
     if (err != hipSuccess) return err;
     const unsigned grid_l = persistent_grid(k_attn_local<D, BETA, BF16>, lds_l, ntiles);

@@ -22,8 +22,6 @@
 
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int BA_THREADS = 256;
 constexpr int BA_CHUNK_BYTES = 32768;   // LDS staging of key rows per chunk
 

@@ -8,6 +8,7 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16-byte register vector
 
 // Validated sizes of one call (host fills it, kernels take it by value).
 struct Shape {
