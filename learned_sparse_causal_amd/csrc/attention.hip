@@ -316,7 +316,9 @@ constexpr int SEG = 1024;          // tokens per prep segment
 constexpr int SCAN_THREADS = 1024;
 constexpr int CHUNK_ROWS = 256;
 
-__global__ __launch_bounds__(256) void k_attn_prep(Shape s, const int32_t *__restrict__ sel,
+constexpr int PREP_THREADS = 1024;
+
+__global__ __launch_bounds__(PREP_THREADS) void k_attn_prep(Shape s, const int32_t *__restrict__ sel,
                                                    int32_t *__restrict__ cnt,
                                                    int32_t *__restrict__ entry_pos,
                                                    int32_t *__restrict__ tile_flag, int nseg) {
@@ -350,8 +352,8 @@ __global__ __launch_bounds__(256) void k_attn_prep(Shape s, const int32_t *__res
         }
     }
     __syncthreads();
-    int32_t *cg = cnt + ((size_t)b * Hkv + g) * NB * nseg;
-    for (int n = threadIdx.x; n < NB; n += blockDim.x) cg[(size_t)n * nseg + seg] = hist[n];
+    int32_t *cg = cnt + (((size_t)b * Hkv + g) * nseg + seg) * NB;   // [b, g][seg][n]
+    for (int n = threadIdx.x; n < NB; n += blockDim.x) cg[n] = hist[n];
 
 }
 
@@ -407,56 +409,64 @@ __global__ __launch_bounds__(256) void k_attn_rotate(Shape s, const void *__rest
     }
 }
 
-constexpr int BIN_WG = 256;
+constexpr int BIN_WG = 64;    // bins per binsum workgroup (one wave)
 
-// Per bin: exclusive prefix over segments; per workgroup of 256 bins: the
+// Per bin: exclusive prefix over segments; per workgroup of BIN_WG bins: the
 // exclusive scan of bin sizes and of 256-row chunk counts, and their totals.
-__global__ __launch_bounds__(BIN_WG) void k_attn_binsum(int nbins, int nseg,
+__global__ __launch_bounds__(BIN_WG) void k_attn_binsum(int nbins, int nseg, int NB,
                                                         const int32_t *__restrict__ cnt,
                                                         int32_t *__restrict__ seg_rel,
                                                         int32_t *__restrict__ bin_local,
                                                         int32_t *__restrict__ chunk_local,
                                                         int32_t *__restrict__ wg_sum) {
-    __shared__ int32_t ps[BIN_WG], pc[BIN_WG];
     const int tid = threadIdx.x;
     const long bin = (long)blockIdx.x * BIN_WG + tid;
     int acc = 0;
     if (bin < nbins) {
-        const int32_t *c = cnt + bin * nseg;
-        int32_t *o = seg_rel + bin * nseg;
-        for (int sg = 0; sg < nseg; ++sg) {
-            const int x = c[sg];
-            o[sg] = acc;
+        // counts are [b, g][seg][n]: consecutive bins of a wave are adjacent
+        const long base = (bin / NB) * nseg * (long)NB + bin % NB;
+        const int32_t *c = cnt + base;
+        int32_t *o = seg_rel + base;
+        int sg = 0;
+        for (; sg + 8 <= nseg; sg += 8) {   // eight loads in flight
+            int x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = c[(long)(sg + u) * NB];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                o[(long)(sg + u) * NB] = acc;
+                acc += x[u];
+            }
+        }
+        for (; sg < nseg; ++sg) {
+            const int x = c[(long)sg * NB];
+            o[(long)sg * NB] = acc;
             acc += x;
         }
     }
     const int nch = (acc + CHUNK_ROWS - 1) / CHUNK_ROWS;
-    ps[tid] = acc;
-    pc[tid] = nch;
-    __syncthreads();
-    for (int off = 1; off < BIN_WG; off <<= 1) {  // inclusive Hillis-Steele scan
-        const int a = tid >= off ? ps[tid - off] : 0;
-        const int c = tid >= off ? pc[tid - off] : 0;
-        __syncthreads();
-        ps[tid] += a;
-        pc[tid] += c;
-        __syncthreads();
+    // inclusive wave scans of the bin sizes and chunk counts
+    int ps = acc, pc = nch;
+#pragma unroll
+    for (int dlt = 1; dlt < WAVE; dlt <<= 1) {
+        const int a = __shfl_up(ps, dlt), c = __shfl_up(pc, dlt);
+        if (tid >= dlt) { ps += a; pc += c; }
     }
     if (bin < nbins) {
-        bin_local[bin] = ps[tid] - acc;
-        chunk_local[bin] = pc[tid] - nch;
+        bin_local[bin] = ps - acc;
+        chunk_local[bin] = pc - nch;
     }
     if (tid == BIN_WG - 1) {
-        wg_sum[2 * blockIdx.x] = ps[tid];
-        wg_sum[2 * blockIdx.x + 1] = pc[tid];
+        wg_sum[2 * blockIdx.x] = ps;
+        wg_sum[2 * blockIdx.x + 1] = pc;
     }
 }
 
-// Exclusive scan of the workgroup totals (one workgroup); the grand totals
-// go after the last workgroup.
+// Exclusive scan of the workgroup totals (one workgroup of 1024 threads,
+// each owning a contiguous run); the grand totals go after the last one.
 __global__ __launch_bounds__(1024) void k_attn_scan(int nwg, int32_t *__restrict__ wg_sum) {
-    __shared__ int32_t ps[1024], pc[1024];
-    const int tid = threadIdx.x;
+    __shared__ int32_t ws[16], wc[16];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
     const int per = (nwg + 1023) / 1024;
     const int lo = min(nwg, tid * per), hi = min(nwg, lo + per);
     int s0 = 0, c0 = 0;
@@ -464,18 +474,23 @@ __global__ __launch_bounds__(1024) void k_attn_scan(int nwg, int32_t *__restrict
         s0 += wg_sum[2 * i];
         c0 += wg_sum[2 * i + 1];
     }
-    ps[tid] = s0;
-    pc[tid] = c0;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int a = tid >= off ? ps[tid - off] : 0;
-        const int c = tid >= off ? pc[tid - off] : 0;
-        __syncthreads();
-        ps[tid] += a;
-        pc[tid] += c;
-        __syncthreads();
+    int ps = s0, pc = c0;
+#pragma unroll
+    for (int dlt = 1; dlt < WAVE; dlt <<= 1) {
+        const int a = __shfl_up(ps, dlt), c = __shfl_up(pc, dlt);
+        if (lane >= dlt) { ps += a; pc += c; }
     }
-    int rs = tid ? ps[tid - 1] : 0, rc = tid ? pc[tid - 1] : 0;
+    if (lane == WAVE - 1) { ws[wv] = ps; wc[wv] = pc; }
+    __syncthreads();
+    int bs = 0, bc = 0, ts = 0, tc = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        bs += w < wv ? ws[w] : 0;
+        bc += w < wv ? wc[w] : 0;
+        ts += ws[w];
+        tc += wc[w];
+    }
+    int rs = bs + ps - s0, rc = bc + pc - c0;
     for (int i = lo; i < hi; ++i) {
         const int a = wg_sum[2 * i], c = wg_sum[2 * i + 1];
         wg_sum[2 * i] = rs;
@@ -483,11 +498,17 @@ __global__ __launch_bounds__(1024) void k_attn_scan(int nwg, int32_t *__restrict
         rs += a;
         rc += c;
     }
-    if (tid == 1023) {
-        wg_sum[2 * nwg] = ps[tid];
-        wg_sum[2 * nwg + 1] = pc[tid];
+    if (tid == 0) {
+        wg_sum[2 * nwg] = ts;
+        wg_sum[2 * nwg + 1] = tc;
     }
 }
+
+// Remote work split: chunk c costs its rows plus CHUNK_OVH (the K/V load and
+// synchronization it brings); workgroup w of the persistent grid takes the
+// chunks [wg_first[w], wg_first[w + 1]) (written by k_attn_scatter).
+constexpr int CHUNK_OVH = 128;
+constexpr int MAX_REMOTE_GRID = 8192;   // bound of the remote kernel's persistent grid
 
 __device__ __forceinline__ int bin_start_of(const int32_t *bin_local, const int32_t *wg_base,
                                             long bin) {
@@ -505,7 +526,8 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
                                                       const int32_t *__restrict__ wg_base,
                                                       const int32_t *__restrict__ seg_rel,
                                                       int32_t *__restrict__ list_q,
-                                                      int4 *__restrict__ chunk_desc) {
+                                                      int4 *__restrict__ chunk_desc,
+                                                      int grid_r, int32_t *__restrict__ wg_first) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < nbins) {
         // descriptors {bin, first row, end row} of the bin's chunks
@@ -516,9 +538,20 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
                                   : wg_base[2 * nwg + 1];
         const int b0 = bin_start_of(bin_local, wg_base, i);
         const int b1 = i + 1 < nb ? bin_start_of(bin_local, wg_base, i + 1) : wg_base[2 * nwg];
+        // remote work split: chunk c costs its rows plus CHUNK_OVH and spans
+        // the cost interval [r0 + OVH c, r1 + OVH (c + 1)); workgroup w starts
+        // at the chunk whose interval holds w * total / grid_r
+        const long rows = wg_base[2 * nwg], nchunks = wg_base[2 * nwg + 1];
+        const long total = rows + (long)CHUNK_OVH * nchunks;
+        if (i == 0 && nchunks == 0)
+            for (int w = 0; w <= grid_r; ++w) wg_first[w] = 0;
         for (int c = c0; c < c1; ++c) {
-            const int r0 = b0 + (c - c0) * CHUNK_ROWS;
-            chunk_desc[c] = make_int4((int)i, r0, min(r0 + CHUNK_ROWS, b1), 0);
+            const int r0 = b0 + (c - c0) * CHUNK_ROWS, r1 = min(r0 + CHUNK_ROWS, b1);
+            chunk_desc[c] = make_int4((int)i, r0, r1, 0);
+            const long pst = r0 + (long)CHUNK_OVH * c, pen = r1 + (long)CHUNK_OVH * (c + 1);
+            const long w_lo = (pst * grid_r + total - 1) / total, w_hi = (pen * grid_r - 1) / total;
+            for (long w = w_lo; w <= w_hi; ++w) wg_first[w] = c;
+            if (c == nchunks - 1) wg_first[grid_r] = (int)nchunks;
         }
     }
     const long n = (long)s.B * s.Hq * s.T * s.R;
@@ -529,7 +562,8 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
     const int t = (int)(route % s.T);
     const int h = (int)((route / s.T) % s.Hq), b = (int)(route / ((long)s.T * s.Hq));
     const long bin = ((long)b * s.Hkv + h / s.G) * s.NB + sel[i];
-    const int at = bin_start_of(bin_local, wg_base, bin) + seg_rel[bin * nseg + t / SEG] + pos;
+    const long sr = ((bin / s.NB) * nseg + t / SEG) * (long)s.NB + bin % s.NB;
+    const int at = bin_start_of(bin_local, wg_base, bin) + seg_rel[sr] + pos;
     list_q[at] = (int32_t)(((long)b * s.T + t) * s.Hq + h);   // row of q_rot
     entry_pos[i] = at;                                         // where its partial will be
 }
@@ -540,34 +574,6 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
 // task after next and the query rows of the next task are in flight while a
 // task computes.  The next chunk's K / V^T (if its bin differs) is staged in
 // registers during the current chunk and written to LDS after it.
-// Work split of the remote kernel: chunk c costs its rows plus CHUNK_OVH (the
-// K/V load and synchronization it brings), so the cost before chunk c is
-// r0(c) + CHUNK_OVH * c.  Workgroup w of `grid` takes the chunks whose cost
-// prefix falls in [w, w + 1) * total / grid; wg_first[w] is its first chunk
-// and wg_first[grid] = nchunks.
-constexpr int CHUNK_OVH = 128;
-constexpr int MAX_REMOTE_GRID = 8192;   // bound of the remote kernel's persistent grid
-
-__global__ __launch_bounds__(256) void k_attn_split(int grid, const int4 *__restrict__ chunk_desc,
-                                                    const int32_t *__restrict__ totals,
-                                                    int32_t *__restrict__ wg_first) {
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;
-    const int rows = totals[0], nchunks = totals[1];
-    if (c == 0 && nchunks == 0)
-        for (int w = 0; w <= grid; ++w) wg_first[w] = 0;
-    if (c >= nchunks) return;
-    const double total = (double)rows + (double)CHUNK_OVH * nchunks;
-    auto owner = [&](int cc) {
-        const double pre = (double)chunk_desc[cc].y + (double)CHUNK_OVH * cc;
-        return min(grid - 1, (int)(pre * grid / total));
-    };
-    const int o = owner(c);
-    const int op = c > 0 ? owner(c - 1) : -1;
-    for (int w = op + 1; w <= o; ++w) wg_first[w] = c;
-    if (c == nchunks - 1)
-        for (int w = o + 1; w <= grid; ++w) wg_first[w] = nchunks;
-}
-
 template <int D, int BETA, bool BF16>
 __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
                                                      const Elem<BF16> *__restrict__ k_rot,
@@ -957,24 +963,22 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
                                    reinterpret_cast<E *>(w.k_rot));
     hipError_t err = ensure_lds(k_attn_prep, (size_t)s.NB * sizeof(int));
     if (err != hipSuccess) return err;
-    k_attn_prep<<<dim3((unsigned)nseg, (unsigned)s.Hkv, (unsigned)s.B), 256,
+    k_attn_prep<<<dim3((unsigned)nseg, (unsigned)s.Hkv, (unsigned)s.B), PREP_THREADS,
                   (size_t)s.NB * sizeof(int), st>>>(s, sel, w.cnt, w.entry_pos, w.tile_flag, nseg);
-    k_attn_binsum<<<dim3((unsigned)nwg), BIN_WG, 0, st>>>(nbins, nseg, w.cnt, w.seg_rel,
+    k_attn_binsum<<<dim3((unsigned)nwg), BIN_WG, 0, st>>>(nbins, nseg, s.NB, w.cnt, w.seg_rel,
                                                           w.bin_local, w.chunk_local, w.wg_sum);
     k_attn_scan<<<1, 1024, 0, st>>>(nwg, w.wg_sum);
-    const long nscat = std::max<long>(nent, nbins);
-    k_attn_scatter<<<dim3((unsigned)((nscat + 255) / 256)), 256, 0, st>>>(
-        s, nseg, nbins, sel, w.entry_pos, w.bin_local, w.chunk_local, w.wg_sum, w.seg_rel,
-        w.list_q, w.chunk_desc);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
     const size_t lds_r = (size_t)((BETA / 64) * (T::K_ELEMS + T::V_ELEMS)) * sizeof(E);
     err = ensure_lds(k_attn_remote<D, BETA, BF16>, lds_r);
     if (err != hipSuccess) return err;
     const unsigned grid_r = std::min<unsigned>(
         persistent_grid(k_attn_remote<D, BETA, BF16>, lds_r, max_chunks(s)), MAX_REMOTE_GRID);
-    k_attn_split<<<dim3((unsigned)((max_chunks(s) + 255) / 256)), 256, 0, st>>>(
-        (int)grid_r, w.chunk_desc, w.wg_sum + 2 * nwg, w.wg_first);
+    const long nscat = std::max<long>(nent, nbins);
+    k_attn_scatter<<<dim3((unsigned)((nscat + 255) / 256)), 256, 0, st>>>(
+        s, nseg, nbins, sel, w.entry_pos, w.bin_local, w.chunk_local, w.wg_sum, w.seg_rel,
+        w.list_q, w.chunk_desc, (int)grid_r, w.wg_first);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
     k_attn_remote<D, BETA, BF16><<<dim3(grid_r), 256, lds_r, st>>>(
         s, reinterpret_cast<const E *>(w.q_rot), reinterpret_cast<const E *>(w.k_rot),
         reinterpret_cast<const E *>(v), w.list_q, w.chunk_desc, w.wg_first, w.part_lse,
