@@ -283,22 +283,22 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
             const float a1 = *reinterpret_cast<const float *>(scl + m.y);
             return a0 + a1;
         };
+        // The list is sorted and a new block's id exceeds every resident's,
+        // so only the new block is compared (strictly: a resident of equal
+        // sigma has the lower id); it takes the first slot it beats and the
+        // slots after it shift down by one.
         auto visit = [&](float sg, int n) {
             if (need & (sg > bs[RM - 1])) {
-                float v = sg;
-                int id = n;
+                bool beat[RM];
 #pragma unroll
-                for (int x = 0; x < RM; ++x) {
-                    // a block pushed down the list meets later blocks of
-                    // equal sigma: the lower block id stays first
-                    const bool sw = (v > bs[x]) | ((v == bs[x]) & (id < bn[x]));
-                    const float ov = bs[x];
-                    const int oi = bn[x];
-                    bs[x] = sw ? v : ov;
-                    bn[x] = sw ? id : oi;
-                    v = sw ? ov : v;
-                    id = sw ? oi : id;
+                for (int x = 0; x < RM; ++x) beat[x] = sg > bs[x];
+#pragma unroll
+                for (int x = RM - 1; x > 0; --x) {
+                    bs[x] = beat[x] ? (beat[x - 1] ? bs[x - 1] : sg) : bs[x];
+                    bn[x] = beat[x] ? (beat[x - 1] ? bn[x - 1] : n) : bn[x];
                 }
+                bs[0] = beat[0] ? sg : bs[0];
+                bn[0] = beat[0] ? n : bn[0];
             }
         };
         constexpr int U = 8;
