@@ -63,7 +63,16 @@ __device__ __forceinline__ void insert(u64 (&lst)[M], u64 k) {
     }
 }
 
-template <int D, int P, int NPRM, int RM, bool BF16>
+// Float offset of the per-wave score areas (after the lists, 16-byte aligned).
+__host__ __device__ constexpr int route_sc_off(int NB, int A) { return (3 * NB + A + 1 + 3) & ~3; }
+
+// Floats of one wave's score area: P*K score rows and a -inf row of 64
+// lanes; with matrix-core scoring it also holds the query transpose.
+__host__ __device__ constexpr int route_wave_floats(int PK, int DS, bool mf) {
+    return mf && 64 * (DS + 4) > (PK + 1) * 64 ? 64 * (DS + 4) : (PK + 1) * 64;
+}
+
+template <int D, int P, int NPRM, int RM, bool BF16, bool MF>
 __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__ q,
                                                const float *__restrict__ cos_t,
                                                const float *__restrict__ sin_t,
@@ -81,11 +90,10 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     int2 *meta_s = reinterpret_cast<int2 *>(lds);                // [NB]: score-row offsets
     int *off_s = reinterpret_cast<int *>(meta_s + NB);           // [A+1]
     int *ent_s = off_s + A + 1;                                  // [NB]
-    float *sc_all = reinterpret_cast<float *>(ent_s + NB);       // [nw][P*K + 1][64]
+    float *sc_all = reinterpret_cast<float *>(lds) + route_sc_off(NB, A);   // [nw][...][64]
     const int lane = lane_id(), wave = threadIdx.x / WAVE;
-    float *sc_s = sc_all + wave * (PK + 1) * WAVE;
+    float *sc_s = sc_all + wave * route_wave_floats(PK, DS, MF);
     const int dummy = PK * WAVE * 4;                             // byte offset of a -inf row
-    sc_s[PK * WAVE + lane] = -INFINITY;
 
     const int h = blockIdx.y, b = blockIdx.z, g = h / s.G;
     const size_t ug = (size_t)b * s.Hkv + g;
@@ -161,6 +169,91 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     // code first on equal scores)
     float tv[P][NPRM];
     int tc[P][NPRM];
+    if constexpr (MF) {
+        // Matrix cores: per component, D[route][code] = sum_k A[route][k]
+        // B[k][code] as a chain of fp32 16x16x4 MFMAs over steps st, with
+        // lane group lg carrying dimension 4 st + lg.  Each MFMA adds its
+        // four products in k order, one rounding each, so the chain is the
+        // fused multiply-add chain in dimension order.  The A operand (the
+        // routes' rotated queries) passes through the wave's score area,
+        // one component at a time; every A fragment is in registers before
+        // the first score is written there.
+        const int lr = lane & 15, lg = lane >> 4;
+        constexpr int MT = WAVE / 16, NS = DS / 4;
+        constexpr int QTS = DS + 4;                      // transpose row stride (floats)
+        float af[P][MT][NS];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+                for (int st = 0; st < NS; st += 4)
+                    *reinterpret_cast<float4 *>(sc_s + lane * QTS + g4 * NS + st) =
+                        make_float4(qr[p * DS + 4 * st + g4], qr[p * DS + 4 * (st + 1) + g4],
+                                    qr[p * DS + 4 * (st + 2) + g4], qr[p * DS + 4 * (st + 3) + g4]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int st = 0; st < NS; st += 4) {
+                    const float4 v4 =
+                        *reinterpret_cast<const float4 *>(sc_s + (mt * 16 + lr) * QTS + lg * NS + st);
+                    af[p][mt][st] = v4.x;
+                    af[p][mt][st + 1] = v4.y;
+                    af[p][mt][st + 2] = v4.z;
+                    af[p][mt][st + 3] = v4.w;
+                }
+        }
+        const int NT = (K + 15) / 16;
+        const float *cbg = cb + (size_t)g * PK * DS;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            for (int nt = 0; nt < NT; ++nt) {
+                // B operand: code nt*16 + lr, dimension 4 st + lg (codebook
+                // rows are small and stay in the caches)
+                const int code = nt * 16 + lr;
+                const float *brow = cbg + (p * K + (code < K ? code : 0)) * DS + lg;
+                float bf[NS];
+#pragma unroll
+                for (int st = 0; st < NS; ++st) bf[st] = code < K ? brow[4 * st] : 0.0f;
+                f32x4 acc[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < NS; ++st)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[p][mt][st], bf[st],
+                                                                       acc[mt], 0, 0, 0);
+                // lane holds routes mt*16 + 4 lg + r of code nt*16 + lr
+                if (code < K) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        *reinterpret_cast<float4 *>(sc_s + (p * K + code) * WAVE + mt * 16 + 4 * lg) =
+                            make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+                }
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+#pragma unroll
+            for (int x = 0; x < NPRM; ++x) { tv[p][x] = -INFINITY; tc[p][x] = -1; }
+#pragma unroll 4
+            for (int c = 0; c < K; ++c) {
+                float v = sc_s[(p * K + c) * WAVE + lane];
+                int cc = c;
+#pragma unroll
+                for (int x = 0; x < NPRM; ++x) {
+                    const bool sw = v > tv[p][x];
+                    const float ov = tv[p][x];
+                    const int oc = tc[p][x];
+                    tv[p][x] = sw ? v : ov;
+                    tc[p][x] = sw ? cc : oc;
+                    v = sw ? ov : v;
+                    cc = sw ? oc : cc;
+                }
+            }
+        }
+    } else {
     const float *cbg = cb + (size_t)g * PK * DS;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -186,6 +279,7 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                 cc = sw ? oc : cc;
             }
         }
+    }
     }
 
     // ---- the n_probes best addresses (keys: sigma, then lower address)
@@ -264,6 +358,8 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
         }
     }
 
+    sc_s[PK * WAVE + lane] = -INFINITY;   // the row unindexed blocks point at
+
     // ---- pool part 2: extension to R blocks, for lanes that need it.  The
     // R best eligible indexed blocks by (sigma desc, block asc), visited in
     // source order; a new block enters only if its sigma beats the R-th best.
@@ -286,9 +382,11 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
         // The list is sorted and a new block's id exceeds every resident's,
         // so only the new block is compared (strictly: a resident of equal
         // sigma has the lower id); it takes the first slot it beats and the
-        // slots after it shift down by one.
+        // slots after it shift down by one.  Short lists are updated without
+        // a branch (lanes that need no extension update a list they never
+        // read).
         auto visit = [&](float sg, int n) {
-            if (need & (sg > bs[RM - 1])) {
+            if (RM <= 2 || (need & (sg > bs[RM - 1]))) {   // short lists: no branch
                 bool beat[RM];
 #pragma unroll
                 for (int x = 0; x < RM; ++x) beat[x] = sg > bs[x];
@@ -379,39 +477,54 @@ __global__ __launch_bounds__(256) void k_route_bypass(Shape s, int32_t *__restri
     for (int r = 0; r < s.R; ++r) out[r] = r < E ? r : -1;
 }
 
-// LDS of one workgroup: per-block score rows and tie words, list offsets,
-// list entries and one score table per wave.
-size_t route_lds(const Shape &s, int waves) {
+// LDS of one workgroup: per-block score-row offsets, list offsets, list
+// entries and one score area per wave.
+size_t route_lds(const Shape &s, int waves, bool mf) {
     const int PK = s.P * s.K;
-    return (size_t)(s.A + 1 + 3 * s.NB) * sizeof(int) +
-           (size_t)(waves * (PK + 1) * WAVE) * sizeof(float);
+    return (size_t)route_sc_off(s.NB, s.A) * sizeof(int) +
+           (size_t)waves * route_wave_floats(PK, s.ds, mf) * sizeof(float);
 }
 
 // Four waves per workgroup unless that overflows the 160 KiB of LDS.
-int route_waves(const Shape &s) {
+int route_waves(const Shape &s, bool mf) {
     int w = 4;
-    while (w > 1 && route_lds(s, w) > 160 * 1024) w /= 2;
+    while (w > 1 && route_lds(s, w, mf) > 160 * 1024) w /= 2;
     return w;
 }
 
-template <int D, int P, int NPRM, int RM, bool BF16>
+template <int D, int P, int NPRM, int RM, bool BF16, bool MF>
 hipError_t launch_t(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
                     const float *cb, const float *kbar, const int32_t *addr,
                     const int32_t *offsets, const int32_t *entries, int32_t *sel,
                     hipStream_t st) {
-    const int waves = route_waves(s);
-    const size_t lds = route_lds(s, waves);
+    const int waves = route_waves(s, MF);
+    const size_t lds = route_lds(s, waves, MF);
     const dim3 grid((unsigned)((s.T + waves * WAVE - 1) / (waves * WAVE)), (unsigned)s.Hq,
                     (unsigned)s.B);
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(k_route<D, P, NPRM, RM, BF16>),
+            reinterpret_cast<const void *>(k_route<D, P, NPRM, RM, BF16, MF>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    k_route<D, P, NPRM, RM, BF16><<<grid, waves * WAVE, lds, st>>>(
+    k_route<D, P, NPRM, RM, BF16, MF><<<grid, waves * WAVE, lds, st>>>(
         s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, sel);
     return hipGetLastError();
+}
+
+// Matrix-core scoring for d = 64, two components, at most 32 codes each.
+template <int D, int P, int NPRM, int RM, bool BF16>
+hipError_t launch_m(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
+                    const float *cb, const float *kbar, const int32_t *addr,
+                    const int32_t *offsets, const int32_t *entries, int32_t *sel,
+                    hipStream_t st) {
+    if constexpr (D == 64 && P == 2) {
+        if (s.K <= 32 && route_lds(s, 1, true) <= 160 * 1024)
+            return launch_t<D, P, NPRM, RM, BF16, true>(s, q, cos_t, sin_t, cb, kbar, addr,
+                                                        offsets, entries, sel, st);
+    }
+    return launch_t<D, P, NPRM, RM, BF16, false>(s, q, cos_t, sin_t, cb, kbar, addr, offsets,
+                                                 entries, sel, st);
 }
 
 template <int D, int P, bool BF16>
@@ -420,15 +533,15 @@ hipError_t launch_sel(const Shape &s, const void *q, const float *cos_t, const f
                       const int32_t *offsets, const int32_t *entries, int32_t *sel,
                       hipStream_t st) {
     if (s.npr <= 2 && s.R <= 2)
-        return launch_t<D, P, 2, 2, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
+        return launch_m<D, P, 2, 2, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
                                           sel, st);
     if (s.npr <= 4 && s.R <= 2)
-        return launch_t<D, P, 4, 2, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
+        return launch_m<D, P, 4, 2, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
                                           sel, st);
     if (s.npr <= 8 && s.R <= 8)
-        return launch_t<D, P, 8, 8, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
+        return launch_m<D, P, 8, 8, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
                                           sel, st);
-    return launch_t<D, P, 16, 16, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
+    return launch_m<D, P, 16, 16, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
                                         sel, st);
 }
 
