@@ -340,9 +340,22 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
         insert(rk, key_of(acc, (uint32_t)(0x7FFFFFFF - n)));
     };
 
+    // ---- candidates (pool members) in canonical order: the part-1 walk,
+    // then the extension's blocks; the first MAXC are kept in registers and
+    // reranked in one batch, the rest (long lists only) afterwards
+    constexpr int MAXC = 8;
+    int cand[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) cand[i] = -1;
+    int nc = 0;
+    auto add = [&](int n) {
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) cand[i] = i == nc ? n : cand[i];
+        ++nc;
+    };
+
     // ---- pool part 1: the eligible prefixes of the n_probes best lists
-    int cnt = 0;
-    if (live) {
+    auto walk_part1 = [&](auto &&fn) {
 #pragma unroll
         for (int x = 0; x < NPRM; ++x) {
             if (x < npr) {
@@ -351,12 +364,13 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                 for (int e = off_s[a]; e < e1; ++e) {
                     const int n = ent_s[e];
                     if (n > last) break;
-                    rerank(n);
-                    ++cnt;
+                    fn(n);
                 }
             }
         }
-    }
+    };
+    int cnt = 0;
+    if (live) walk_part1([&](int n) { add(n); ++cnt; });
 
     sc_s[PK * WAVE + lane] = -INFINITY;   // the row unindexed blocks point at
 
@@ -367,11 +381,11 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     // block rather than address (an exact score tie at the pool boundary).
     // RM - R sentinel slots never move.
     const bool need = live && cnt < R;
-    if (__ballot(need) != 0ull) {
-        float bs[RM];
-        int bn[RM];
+    float bs[RM];
+    int bn[RM];
 #pragma unroll
-        for (int x = 0; x < RM; ++x) { bs[x] = x < RM - R ? INFINITY : -INFINITY; bn[x] = -1; }
+    for (int x = 0; x < RM; ++x) { bs[x] = x < RM - R ? INFINITY : -INFINITY; bn[x] = -1; }
+    if (__ballot(need) != 0ull) {
         const char *scl = reinterpret_cast<const char *>(sc_s + lane);
         auto sigma = [&](int2 m) {
             const float a0 = *reinterpret_cast<const float *>(scl + m.x);
@@ -412,37 +426,78 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
             for (int u = 0; u < U; ++u) visit(sg[u], n + u);
         }
         for (; n <= last; ++n) visit(sigma(meta_s[n]), n);
-        if (need) {
-            // address of an indexed block, from its score-row offsets
-            auto addr_of = [&](int nn) {
-                const int2 m = meta_s[nn];
-                const int c0 = m.x / (WAVE * 4);
-                return P == 1 ? c0 : c0 * K + (m.y / (WAVE * 4) - K);
-            };
-            // does (sigma, address) rank after the n_probes-th address?
-            auto after_tau = [&](float sg, int a) {
-                return (sg < tau_v) | ((sg == tau_v) & (a > tau_a));
-            };
-            // the R best blocks that rank after tau (the others are in part 1)
+    }
+    // address of an indexed block, from its score-row offsets
+    auto addr_of = [&](int nn) {
+        const int2 m = meta_s[nn];
+        const int c0 = m.x / (WAVE * 4);
+        return P == 1 ? c0 : c0 * K + (m.y / (WAVE * 4) - K);
+    };
+    // does (sigma, address) rank after the n_probes-th address?
+    auto after_tau = [&](float sg, int a) {
+        return (sg < tau_v) | ((sg == tau_v) & (a > tau_a));
+    };
+    // the extension's pool members: the R best blocks that rank after tau
+    // (the others are in part 1), then the blocks of the R-th block's
+    // address after it (they tie with it)
+    auto walk_ext = [&](auto &&fn) {
+        if (!need) return;
 #pragma unroll
-            for (int x = 0; x < RM; ++x) {
-                if (x < RM - R || bn[x] < 0) continue;
-                if (after_tau(bs[x], addr_of(bn[x]))) rerank(bn[x]);
-            }
-            // blocks of the R-th block's address after it tie with it
-            const int nR = bn[RM - 1];
-            if (nR >= 0) {
-                const int aR = addr_of(nR);
-                if (after_tau(bs[RM - 1], aR)) {
-                    const int e1 = off_s[aR + 1];
-                    for (int e = off_s[aR]; e < e1; ++e) {
-                        const int nn = ent_s[e];
-                        if (nn > last) break;
-                        if (nn > nR) rerank(nn);
-                    }
+        for (int x = 0; x < RM; ++x) {
+            if (x < RM - R || bn[x] < 0) continue;
+            if (after_tau(bs[x], addr_of(bn[x]))) fn(bn[x]);
+        }
+        const int nR = bn[RM - 1];
+        if (nR >= 0) {
+            const int aR = addr_of(nR);
+            if (after_tau(bs[RM - 1], aR)) {
+                const int e1 = off_s[aR + 1];
+                for (int e = off_s[aR]; e < e1; ++e) {
+                    const int nn = ent_s[e];
+                    if (nn > last) break;
+                    if (nn > nR) fn(nn);
                 }
             }
         }
+    };
+    walk_ext(add);
+
+    // ---- rerank: two candidates at a time, their summaries loaded together
+    // (indexes clamped so the loads of empty slots stay in bounds)
+#pragma unroll
+    for (int i = 0; i < MAXC; i += 2) {
+        if (__ballot(i < nc) == 0ull) break;
+        const int n0 = cand[i] >= 0 ? cand[i] : 0, n1 = cand[i + 1] >= 0 ? cand[i + 1] : 0;
+        const float *k0 = kb + (size_t)n0 * D, *k1 = kb + (size_t)n1 * D;
+        float4 v0[D / 4], v1[D / 4];
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) {
+            v0[j] = reinterpret_cast<const float4 *>(k0)[j];
+            v1[j] = reinterpret_cast<const float4 *>(k1)[j];
+        }
+        float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) {
+            acc0 = __builtin_fmaf(qr[4 * j], v0[j].x, acc0);
+            acc0 = __builtin_fmaf(qr[4 * j + 1], v0[j].y, acc0);
+            acc0 = __builtin_fmaf(qr[4 * j + 2], v0[j].z, acc0);
+            acc0 = __builtin_fmaf(qr[4 * j + 3], v0[j].w, acc0);
+            acc1 = __builtin_fmaf(qr[4 * j], v1[j].x, acc1);
+            acc1 = __builtin_fmaf(qr[4 * j + 1], v1[j].y, acc1);
+            acc1 = __builtin_fmaf(qr[4 * j + 2], v1[j].z, acc1);
+            acc1 = __builtin_fmaf(qr[4 * j + 3], v1[j].w, acc1);
+        }
+        if (i < nc) insert(rk, key_of(acc0, (uint32_t)(0x7FFFFFFF - n0)));
+        if (i + 1 < nc) insert(rk, key_of(acc1, (uint32_t)(0x7FFFFFFF - n1)));
+    }
+    if (__ballot(nc > MAXC) != 0ull) {   // candidates past the register batch
+        int k = 0;
+        auto late = [&](int n) {
+            if (k >= MAXC) rerank(n);
+            ++k;
+        };
+        if (live) walk_part1(late);
+        walk_ext(late);
     }
 
     // ---- emit the kept blocks ascending, -1 padded
