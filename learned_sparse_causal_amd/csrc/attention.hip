@@ -719,40 +719,61 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     // again.
     const int nitems = s.B * s.Hq * ntt;
     const int per = (nitems + gridDim.x - 1) / gridDim.x;
-    const int i_end = min(nitems, (int)blockIdx.x * per + per);
+    const int i_beg = blockIdx.x * per, i_end = min(nitems, i_beg + per);
     int resident_bh = -1, resident_kb = -1;
-    for (int item = blockIdx.x * per; item < i_end; ++item) {
+    const int lane = lane_id(), wave = threadIdx.x / WAVE, lr = lane & 15, lg = lane >> 4;
+    const int R = s.R;
+
+    // Merge inputs of this lane's query for the first RP slots, one tile
+    // ahead: entry positions are fetched when the previous tile starts, the
+    // log-sum-exps and partial rows when its attention is done.  (Prep
+    // leaves every slot of a uniform tile at -1, so no tile flag is needed.)
+    constexpr int RP = 2;
+    int ep_c[RP], ep_n[RP];
+    float lse_c[RP], lse_n[RP];
+    PartChunks<D, BF16> o_c[RP], o_n[RP];
+    auto fetch_ep = [&](int it) {
+        const long rt = it < i_end ? (long)(it / ntt) * s.T + (ntt - 1 - it % ntt) * 64 +
+                                         wave * 16 + lr
+                                   : 0;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) ep_n[r] = (it < i_end && r < R) ? entry_pos[rt * R + r] : -1;
+    };
+    auto fetch_part = [&]() {
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            lse_n[r] = ep_n[r] >= 0 ? part_lse[ep_n[r]] : 0.0f;
+            if (ep_n[r] >= 0) o_n[r].load(part_o + (size_t)ep_n[r] * D, lg);
+            else o_n[r].zero();
+        }
+    };
+    auto advance = [&]() {
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            ep_c[r] = ep_n[r];
+            lse_c[r] = lse_n[r];
+            o_c[r] = o_n[r];
+        }
+    };
+    fetch_ep(i_beg);
+    fetch_part();
+    advance();
+    for (int item = i_beg; item < i_end; ++item) {
     __syncthreads();   // the previous item is done with LDS
     const int tt = ntt - 1 - item % ntt;
     const int bh = item / ntt;
     const int h = bh % s.Hq, b = bh / s.Hq, g = h / s.G;
-    const int t0 = tt * 64, qb = t0 / BETA, R = s.R, L = s.L;
+    const int t0 = tt * 64, qb = t0 / BETA, L = s.L;
     const int T_ = s.T, Hkv = s.Hkv, Hq = s.Hq;
     const long tile = (long)bh * ntt + tt;
     const bool uni = tile_flag[tile] != 0;
     const long route0 = (long)bh * T_ + t0;
 
-    const int lane = lane_id(), wave = threadIdx.x / WAVE, lr = lane & 15, lg = lane >> 4;
     const int tq = t0 + wave * 16 + lr;  // this lane's query position
     QFrags<D, BF16> qst;
     qst.issue(q_rot, (((size_t)b * T_ + tq) * Hq + h) * D, true);
-    // merge inputs of this lane's query, in flight from the start
     const long route = route0 + wave * 16 + lr;
-    constexpr int RP = 4;   // slots whose partial state is prefetched
-    int ep_pre[RP];
-    float lse_pre[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) ep_pre[r] = (!uni && r < R) ? entry_pos[route * R + r] : -1;
-#pragma unroll
-    for (int r = 0; r < RP; ++r) lse_pre[r] = ep_pre[r] >= 0 ? part_lse[ep_pre[r]] : 0.0f;
-    // the partial outputs of the first RPO slots, in flight from the start
-    constexpr int RPO = 2;
-    PartChunks<D, BF16> o_pre[RPO];
-#pragma unroll
-    for (int r = 0; r < RPO; ++r) {
-        if (ep_pre[r] >= 0) o_pre[r].load(part_o + (size_t)ep_pre[r] * D, lg);
-        else o_pre[r].zero();
-    }
+    fetch_ep(item + 1);   // the next tile's entry positions, in flight
     if (uni) {  // shared remote blocks of the tile: valid first occurrences of row 0
         const int32_t *row0 = sel + route0 * R;
         for (int r = threadIdx.x; r < R; r += blockDim.x) {
@@ -834,6 +855,8 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
         kb_cur = kb_next;
     }
 
+    fetch_part();   // the next tile's partial states, in flight during the merge
+
     // merge: local (and shared) part, then the remote partials in slot order
     const float lse = m + __builtin_amdgcn_logf(l);
     const float inv = 1.0f / l;
@@ -844,8 +867,8 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
         for (int r = 0; r < 4; ++r) acc[dt][r] = o[dt][r] * inv;
     if (!uni) {
         const int32_t *ep = entry_pos + route * R;
-        auto ep_at = [&](int r) { return r < RP ? ep_pre[r] : ep[r]; };
-        auto lse_at = [&](int r) { return r < RP ? lse_pre[r] : part_lse[ep[r]]; };
+        auto ep_at = [&](int r) { return r < RP ? ep_c[r] : ep[r]; };
+        auto lse_at = [&](int r) { return r < RP ? lse_c[r] : part_lse[ep[r]]; };
         float M = lse;
         for (int r = 0; r < R; ++r)
             if (ep_at(r) >= 0) M = fmaxf(M, lse_at(r));
@@ -855,18 +878,18 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[dt][r] *= wsum;
 #pragma unroll
-        for (int r = 0; r < RPO; ++r) {   // prefetched slots (static indexes)
-            if (r >= R || ep_pre[r] < 0) continue;
-            const float w = __builtin_amdgcn_exp2f(lse_pre[r] - M);
+        for (int r = 0; r < RP; ++r) {   // prefetched slots (static indexes)
+            if (r >= R || ep_c[r] < 0) continue;
+            const float w = __builtin_amdgcn_exp2f(lse_c[r] - M);
             wsum += w;
             float x[D / 16][4];
-            o_pre[r].unpack(x);
+            o_c[r].unpack(x);
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
         }
-        for (int r = RPO; r < R; ++r) {
+        for (int r = RP; r < R; ++r) {
             if (ep_at(r) < 0) continue;
             const long e = ep_at(r);
             const float w = __builtin_amdgcn_exp2f(lse_at(r) - M);
@@ -906,6 +929,7 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
                 *reinterpret_cast<const u32x4 *>(stg + rr * OS + d0);
         }
     }
+    advance();
     }
 }
 
