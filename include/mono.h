@@ -95,7 +95,13 @@ typedef struct {
 } mono_index;
 
 /* Which call a workspace is for. */
-enum { MONO_WS_BUILD = 0, MONO_WS_ROUTE = 1, MONO_WS_ATTENTION = 2, MONO_WS_MIXER = 3 };
+enum {
+    MONO_WS_BUILD = 0,
+    MONO_WS_ROUTE = 1,
+    MONO_WS_ATTENTION = 2,
+    MONO_WS_MIXER = 3,
+    MONO_WS_DENSE = 4
+};
 
 /* Bytes of workspace the call `which` needs for `cfg` (0 if it needs none or
  * if cfg is invalid; MONO_WS_MIXER includes q, k, v, the index, the selection
@@ -168,6 +174,23 @@ mono_status mono_selected_attention(const mono_config *cfg, const void *q, const
                                     const void *v, const float *rope_cos, const float *rope_sin,
                                     const int32_t *sel, void *out, void *ws, size_t ws_bytes,
                                     void *stream);
+
+/* Dense causal attention, the baseline the routed path is measured against
+ * (news page, section "What to Watch": a comparison with dense
+ * FlashAttention-style kernels is the decisive systems test; report page,
+ * section "Evidence": with every remote block selected the mixer equals
+ * dense causal softmax).
+ *   q   [B][T][Hq][d], k, v [B][T][Hkv][d]  dtype, un-rotated q and k
+ *   out [B][T][Hq][d] dtype
+ * Query t attends to every token s <= t with logits <rot(q_t), rot(k_s)> /
+ * sqrt(d) and fp32 softmax: the result of mono_selected_attention when every
+ * query selects all of its eligible blocks.  Only batch, seq_len, head
+ * counts, head_dim and dtype are used; the other fields of cfg are validated
+ * as for every call, so the routed path's config can be passed unchanged.
+ * Workspace: MONO_WS_DENSE (the rotated q and k). */
+mono_status mono_dense_attention(const mono_config *cfg, const void *q, const void *k,
+                                 const void *v, const float *rope_cos, const float *rope_sin,
+                                 void *out, void *ws, size_t ws_bytes, void *stream);
 
 /* The whole mixer (report page, "Mixer" and Figure 1): stateless, normalized
  * stream in, attention delta of the same shape out.

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmono.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "mono.h")
 
 MONO_F32, MONO_BF16 = 0, 1
-WS_BUILD, WS_ROUTE, WS_ATTENTION, WS_MIXER = 0, 1, 2, 3
+WS_BUILD, WS_ROUTE, WS_ATTENTION, WS_MIXER, WS_DENSE = 0, 1, 2, 3, 4
 STATUS = {0: "MONO_OK", 1: "MONO_ERR_NULL", 2: "MONO_ERR_SHAPE", 3: "MONO_ERR_UNSUPPORTED",
           4: "MONO_ERR_WORKSPACE", 5: "MONO_ERR_HIP"}
 
@@ -58,12 +58,13 @@ def load_library(path=LIB_PATH):
     lib.mono_build_index.argtypes = [cfgp, P, P, P, P, idxp, P, S, P]
     lib.mono_route.argtypes = [cfgp, P, P, P, P, idxp, P, P, S, P]
     lib.mono_selected_attention.argtypes = [cfgp, P, P, P, P, P, P, P, P, S, P]
+    lib.mono_dense_attention.argtypes = [cfgp, P, P, P, P, P, P, P, S, P]
     lib.mono_mixer_forward.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, S, P]
     lib.mono_mixer_layout.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
     lib.mono_status_string.argtypes = [I]
     lib.mono_status_string.restype = ctypes.c_char_p
     for f in ("mono_rope_table", "mono_build_index", "mono_route", "mono_selected_attention",
-              "mono_mixer_forward", "mono_mixer_layout"):
+              "mono_dense_attention", "mono_mixer_forward", "mono_mixer_layout"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -213,6 +214,26 @@ def selected_attention(cfg, q, k, v, rope_cos, rope_sin, sel, out=None, ws=None)
     _check(load_library().mono_selected_attention(ctypes.byref(c), *args,
                                                   ws.data_ptr() if ws is not None else None,
                                                   nws, _stream()))
+    return out
+
+
+def dense_attention(cfg, q, k, v, rope_cos, rope_sin, out=None, ws=None):
+    """mono_dense_attention: returns out [B, T, Hq, d] in the activation dtype."""
+    torch = _torch()
+    c = make_config(cfg)
+    dt = _act_dtype(cfg)
+    if out is None:
+        out = torch.empty((cfg.B, cfg.T, cfg.Hq, cfg.d), dtype=dt, device="cuda")
+    ws, nws = _workspace(cfg, WS_DENSE, ws)
+    args = (_need(q, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "q"),
+            _need(k, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "k"),
+            _need(v, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "v"),
+            _need(rope_cos, (cfg.T, cfg.d // 2), torch.float32, "rope_cos"),
+            _need(rope_sin, (cfg.T, cfg.d // 2), torch.float32, "rope_sin"),
+            _need(out, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "out"))
+    _check(load_library().mono_dense_attention(ctypes.byref(c), *args,
+                                               ws.data_ptr() if ws is not None else None,
+                                               nws, _stream()))
     return out
 
 

@@ -933,6 +933,216 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Dense causal attention: every query attends to every key at or before it.
+// The news page (section "What to Watch") names the comparison against dense
+// FlashAttention-style kernels as the decisive systems test; this is the
+// dense side of that comparison, on the same rotation pass and tile step as
+// the selected-set kernels.
+
+// One wave, NG groups of 16 queries (qf[g]: B fragments of Q^T as in
+// attend64) against 64 keys; each K and V^T fragment read from LDS serves
+// every group.  MASK: keys after a lane's query (qlim[g]) are masked.
+template <int D, bool BF16, bool MASK, int NG>
+__device__ __forceinline__ void attend64_groups(const Frag8<BF16> (&qf)[NG][D / 32],
+                                                const Elem<BF16> *Ks, const Elem<BF16> *Vt,
+                                                int key0, const int (&qlim)[NG],
+                                                f32x4 (&o)[NG][D / 16], float (&m)[NG],
+                                                float (&l)[NG]) {
+    using T = Tile<D, BF16>;
+    const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
+    f32x4 st[NG][4];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) st[g][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const Frag8<BF16> kf = lds_frag8(Ks + (mt * 16 + lr) * T::QS + 32 * c + 8 * lg);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) mma32(st[g][mt], kf, qf[g][c]);
+        }
+    }
+    Frag8<BF16> pf[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float mx = m[g];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (MASK) {
+                    const int key = key0 + mt * 16 + 4 * lg + r;
+                    st[g][mt][r] = key <= qlim[g] ? st[g][mt][r] : -INFINITY;
+                }
+                mx = fmaxf(mx, st[g][mt][r]);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool none = mx == -INFINITY;   // no key of this row seen yet
+        const float msub = none ? 0.0f : mx;
+        float p[4][4];
+        float ps = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[mt][r] = __builtin_amdgcn_exp2f(st[g][mt][r] - msub);
+                ps += p[mt][r];
+            }
+        }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m[g] - mx);   // exp2(-inf) = 0
+        l[g] = l[g] * alpha + ps;
+        if (!none) m[g] = mx;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[g][dt] *= alpha;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const float pv[8] = {p[2 * c][0], p[2 * c][1], p[2 * c][2], p[2 * c][3],
+                                 p[2 * c + 1][0], p[2 * c + 1][1], p[2 * c + 1][2], p[2 * c + 1][3]};
+            pf[g][c] = reg_frag8<BF16>(pv);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const Elem<BF16> *vr = Vt + (dt * 16 + lr) * T::VS + 32 * c + 4 * lg;
+            const Frag8<BF16> vf = lds_frag4x2(vr, vr + 16);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) mma32(o[g][dt], vf, pf[g][c]);
+        }
+    }
+}
+
+constexpr int DENSE_NG = 2;                      // 16-query groups per wave
+constexpr int DENSE_ROWS = 4 * 16 * DENSE_NG;    // queries per workgroup (4 waves)
+
+template <int D, bool BF16>
+constexpr size_t dense_lds_bytes() {
+    return (size_t)2 * (Tile<D, BF16>::K_ELEMS + Tile<D, BF16>::V_ELEMS) * sizeof(Elem<BF16>);
+}
+
+// One workgroup per (batch, q-head, DENSE_ROWS-query tile).  Key tiles of 64
+// are visited in ascending order through two LDS buffers: the next tile's
+// loads are issued into registers before the current tile's compute and
+// written to the other buffer after it, one barrier per tile.  The tiles
+// that reach past a wave's first query take the causal mask; tiles wholly
+// after a wave's last query are skipped by that wave.  Work items are dealt
+// so that each XCD runs whole heads, heaviest (latest) tiles first: the
+// workgroups of one head sweep its keys from the start at about the same
+// pace and share them in that XCD's L2.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_dense(Shape s, const Elem<BF16> *__restrict__ q_rot,
+                                               const Elem<BF16> *__restrict__ k_rot,
+                                               const Elem<BF16> *__restrict__ v,
+                                               Elem<BF16> *__restrict__ out) {
+    using T = Tile<D, BF16>;
+    using E = Elem<BF16>;
+    constexpr int NG = DENSE_NG;
+    extern __shared__ __align__(16) unsigned char smem[];
+    E *buf = reinterpret_cast<E *>(smem);        // 2 x [K tile | V^T tile]
+    constexpr int BUF = T::K_ELEMS + T::V_ELEMS;
+
+    const int T_ = s.T, Hq = s.Hq, Hkv = s.Hkv;
+    const int ntq = (T_ + DENSE_ROWS - 1) / DENSE_ROWS;
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = item / ntq, tq = ntq - 1 - item % ntq;
+    const int h = bh % Hq, b = bh / Hq, g = h / s.G;
+    const int q0 = tq * DENSE_ROWS;
+    const int nkt = min(T_, q0 + DENSE_ROWS) / 64;   // key tiles 0 .. nkt-1 (T % 64 == 0)
+    const int lane = lane_id(), wave = threadIdx.x / WAVE, lr = lane & 15, lg = lane >> 4;
+    const int w0 = q0 + wave * 16 * NG;              // the wave's first query
+    const bool wave_rows = w0 < T_;                  // T % 64 == 0: all or none of its rows
+
+    int qlim[NG];
+    QFrags<D, BF16> qst[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        qlim[gi] = w0 + gi * 16 + lr;
+        qst[gi].issue(q_rot, (((size_t)b * T_ + qlim[gi]) * Hq + h) * D, wave_rows);
+    }
+    RowStager<D, BF16> kst;
+    VtStager<D, BF16> vst;
+    auto issue_kv = [&](int kt) {
+        const int kb0 = kt * 64;
+        kst.issue(k_rot, [&](int r, size_t &off) {
+            off = (((size_t)b * T_ + kb0 + r) * Hkv + g) * D;
+            return true;
+        });
+        vst.issue(v, (((size_t)b * T_ + kb0) * Hkv + g) * D, (size_t)Hkv * D);
+    };
+    issue_kv(0);
+    Frag8<BF16> qf[NG][D / 32];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) qst[gi].get(qf[gi]);
+    kst.commit(buf);
+    vst.commit(buf + T::K_ELEMS);
+    __syncthreads();
+
+    f32x4 o[NG][D / 16];
+    float m[NG], l[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        m[gi] = -INFINITY;
+        l[gi] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[gi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int kt = 0; kt < nkt; ++kt) {
+        if (kt + 1 < nkt) issue_kv(kt + 1);    // in flight during this tile's compute
+        const E *Ks = buf + (kt & 1) * BUF;
+        const int key0 = kt * 64;
+        if (wave_rows && key0 <= w0 + 16 * NG - 1) {
+            if (key0 + 63 > w0)
+                attend64_groups<D, BF16, true, NG>(qf, Ks, Ks + T::K_ELEMS, key0, qlim, o, m, l);
+            else
+                attend64_groups<D, BF16, false, NG>(qf, Ks, Ks + T::K_ELEMS, key0, qlim, o, m, l);
+        }
+        if (kt + 1 < nkt) {
+            E *nb = buf + ((kt + 1) & 1) * BUF;   // last read in the previous tile
+            kst.commit(nb);
+            vst.commit(nb + T::K_ELEMS);
+        }
+        __syncthreads();
+    }
+    if (!wave_rows) return;
+    // output rows through a staging area in the wave's share of buffer 0 (the
+    // barrier after the last tile ends every read of it): each lane stores 16
+    // contiguous bytes, a store instruction covers 64 bytes of 16 rows
+    constexpr int VE = 16 / sizeof(E);
+    constexpr int OS = D + VE;
+    static_assert(4 * 16 * OS <= 2 * BUF, "staging fits in the tile buffers");
+    E *stg = buf + wave * 16 * OS;
+    const int rr = lane >> 2, qq = lane & 3;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const float inv = 1.0f / l[gi];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const float x[4] = {o[gi][dt][0] * inv, o[gi][dt][1] * inv, o[gi][dt][2] * inv,
+                                o[gi][dt][3] * inv};
+            store4(stg + lr * OS + dt * 16 + 4 * lg, x);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        E *orow = out + (((size_t)b * T_ + w0 + gi * 16 + rr) * Hq + h) * D;
+#pragma unroll
+        for (int j = 0; j < D / (4 * VE); ++j) {
+            const int d0 = j * 4 * VE + qq * VE;
+            *reinterpret_cast<u32x4 *>(orow + d0) =
+                *reinterpret_cast<const u32x4 *>(stg + rr * OS + d0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // reads done before the next group's writes
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 template <typename F>
 hipError_t ensure_lds(F *fn, size_t bytes) {
     if (bytes <= 65536) return hipSuccess;
@@ -946,7 +1156,7 @@ template <typename F>
 unsigned persistent_grid(F *fn, size_t lds, long items) {
     int dev = 0, cus = 256, per_cu = 1;
     if (hipGetDevice(&dev) == hipSuccess)
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn),
                                                      256, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
@@ -1019,7 +1229,51 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     return hipGetLastError();
 }
 
+template <int D, bool BF16>
+hipError_t run_dense(const Shape &s, const void *q, const void *k, const void *v,
+                     const float *cos_t, const float *sin_t, void *out, void *q_rot, void *k_rot,
+                     hipStream_t st) {
+    using E = Elem<BF16>;
+    const long rot_tasks = (long)s.B * s.T * (s.Hq + s.Hkv) * (D / 8);
+    k_attn_rotate<D, BF16><<<dim3((unsigned)std::min<long>((rot_tasks + 255) / 256, 65536L)), 256, 0,
+                             st>>>(s, q, k, cos_t, sin_t, reinterpret_cast<E *>(q_rot),
+                                   reinterpret_cast<E *>(k_rot));
+    const size_t lds = dense_lds_bytes<D, BF16>();
+    hipError_t err = ensure_lds(k_dense<D, BF16>, lds);
+    if (err != hipSuccess) return err;
+    const long items = (long)s.B * s.Hq * ((s.T + DENSE_ROWS - 1) / DENSE_ROWS);
+    k_dense<D, BF16><<<dim3((unsigned)items), 256, lds, st>>>(
+        s, reinterpret_cast<const E *>(q_rot), reinterpret_cast<const E *>(k_rot),
+        reinterpret_cast<const E *>(v), reinterpret_cast<E *>(out));
+    return hipGetLastError();
+}
+
 }  // namespace
+
+// Workspace layout of the dense call: rotated q, rotated k.
+size_t dense_ws_layout(const Shape &s, size_t *off) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t esz = s.dtype == 1 ? 2 : 4;
+    size_t p = 0;
+    off[0] = p; p = al(p + (size_t)s.B * s.T * s.Hq * s.d * esz);
+    off[1] = p; p = al(p + (size_t)s.B * s.T * s.Hkv * s.d * esz);
+    return p;
+}
+
+hipError_t launch_dense(const Shape &s, const void *q, const void *k, const void *v,
+                        const float *cos_t, const float *sin_t, void *out, void *ws,
+                        hipStream_t st) {
+    size_t off[2];
+    dense_ws_layout(s, off);
+    unsigned char *base = reinterpret_cast<unsigned char *>(ws);
+    void *qr = base + off[0], *kr = base + off[1];
+    const bool bf = s.dtype == 1;
+    if (s.d == 64)
+        return bf ? run_dense<64, true>(s, q, k, v, cos_t, sin_t, out, qr, kr, st)
+                  : run_dense<64, false>(s, q, k, v, cos_t, sin_t, out, qr, kr, st);
+    return bf ? run_dense<128, true>(s, q, k, v, cos_t, sin_t, out, qr, kr, st)
+              : run_dense<128, false>(s, q, k, v, cos_t, sin_t, out, qr, kr, st);
+}
 
 // Workspace layout of the attention call (byte offsets, 256-aligned).
 size_t attention_ws_layout(const Shape &s, size_t *off) {

@@ -25,6 +25,10 @@ size_t attention_ws_layout(const Shape &s, size_t *off);
 hipError_t launch_attention(const Shape &s, const void *q, const void *k, const void *v,
                             const float *cos_t, const float *sin_t, const int32_t *sel, void *out,
                             void *ws, hipStream_t st);
+size_t dense_ws_layout(const Shape &s, size_t *off);
+hipError_t launch_dense(const Shape &s, const void *q, const void *k, const void *v,
+                        const float *cos_t, const float *sin_t, void *out, void *ws,
+                        hipStream_t st);
 hipError_t launch_gemm(int bf16, int M, int N, int Kd, const void *A, const void *Bm, void *C,
                        hipStream_t st);
 hipError_t launch_gemm_qkv(int bf16, int M, int N, int Kd, const void *A, const void *Bm, void *q,
@@ -130,6 +134,8 @@ size_t mono_workspace_bytes(const mono_config *cfg, int which) {
             return attention_ws_layout(s, off);
         case MONO_WS_MIXER:
             return mixer_layout(s, off);
+        case MONO_WS_DENSE:
+            return dense_ws_layout(s, off);
         default:
             return 0;
     }
@@ -193,6 +199,19 @@ mono_status mono_selected_attention(const mono_config *cfg, const void *q, const
     if (ws_bytes < attention_ws_layout(s, off)) return MONO_ERR_WORKSPACE;
     return hip_status(launch_attention(s, q, k, v, rope_cos, rope_sin, sel, out, ws,
                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+mono_status mono_dense_attention(const mono_config *cfg, const void *q, const void *k,
+                                 const void *v, const float *rope_cos, const float *rope_sin,
+                                 void *out, void *ws, size_t ws_bytes, void *stream) {
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!q || !k || !v || !rope_cos || !rope_sin || !out || !ws) return MONO_ERR_NULL;
+    size_t off[2];
+    if (ws_bytes < dense_ws_layout(s, off)) return MONO_ERR_WORKSPACE;
+    return hip_status(launch_dense(s, q, k, v, rope_cos, rope_sin, out, ws,
+                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
 mono_status mono_mixer_layout(const mono_config *cfg, size_t *offsets_out) {

@@ -85,6 +85,8 @@ def test_workspace_sizes(lib):
         assert attn >= nent * (cfg.d * es + 12)
         mix = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_MIXER)
         assert mix > attn
+        dense = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_DENSE)
+        assert dense >= cfg.B * cfg.T * (cfg.Hq + cfg.Hkv) * cfg.d * es
         off = binding.mixer_layout(cfg)
         assert off == sorted(off) and all(o % 256 == 0 for o in off)
     bad = binding.make_config(configs.SMALL)
@@ -105,4 +107,9 @@ def test_attention_and_mixer_argument_errors(lib):
     m.width = 100                                                         # Hq*d != W
     assert lib.mono_mixer_forward(ctypes.byref(m), one, one, one, one, one, one, one, None, one,
                                   1 << 40, None) == 2
+    need = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_DENSE)
+    assert lib.mono_dense_attention(ctypes.byref(c), one, one, one, one, one, None, one, need,
+                                    None) == 1
+    assert lib.mono_dense_attention(ctypes.byref(c), one, one, one, one, one, one, one, need - 1,
+                                    None) == 4
     assert lib.mono_status_string(4) == b"workspace too small"
