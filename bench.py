@@ -7,10 +7,12 @@ workload at T = 32768: batch 1, 16 heads, d 64, block 64, 1024 addresses,
 capacity 64, 4 probes, R = 2 remote + 2 local blocks, bf16).  Prints one JSON
 line: tokens/s, the dominant kernel's roofline (its duration taken from HIP
 events recorded around its launches inside the timed steps), the per-stage
-floors, the 4K-32K sweep exponent and the CPU oracle timed on the host cores.
+floors, the 4K-32K sweep exponent, the routed step against the dense causal
+attention kernel (mono_dense_attention) at 4K-64K tokens, and the CPU oracle
+timed on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-cpu-baseline]
-                    [--copy-calibration]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-dense]
+                    [--no-cpu-baseline] [--copy-calibration]
 
 --copy-calibration runs a plain 256 MiB device copy before the steps; hardware
 counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -122,6 +124,32 @@ def run_gpu(cfg, steps, warmup):
     return wall_ms, stage, step_us, stats, sel
 
 
+def time_dense(cfg, reps=3, warmup=1):
+    """mono_dense_attention on the same inputs as the routed step: median of
+    `reps` calls timed with HIP events on the launch stream (ms)."""
+    import torch
+    from learned_sparse_causal_amd import binding, synth
+    d = synth.qkv_device(cfg)
+    cos, sin = binding.device_rope(cfg)
+    out = torch.empty((cfg.B, cfg.T, cfg.Hq, cfg.d), dtype=d["q"].dtype, device="cuda")
+    ws = torch.empty(binding.workspace_bytes(cfg, binding.WS_DENSE), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        binding.dense_attention(cfg, d["q"], d["k"], d["v"], cos, sin, out, ws)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        binding.dense_attention(cfg, d["q"], d["k"], d["v"], cos, sin, out, ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    return float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+
+
+def dense_flops(cfg):
+    """Causal dense attention: 2 d flops for q.k and 2 d for p.v per (query, key <= query)."""
+    return 4.0 * cfg.d * cfg.B * cfg.Hq * cfg.T * (cfg.T + 1) / 2
+
+
 def measured_traffic(kernel):
     """Bytes per launch from the committed counter summary, or None if there is
     none or the kernel's source changed since it was taken."""
@@ -171,6 +199,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the routed attention path is built and timed on a "
@@ -216,15 +245,33 @@ def main():
         floors_us={k: v * 1e6 for k, v in floors.items()},
         index=stats,
     )
+    routed_ms = {}
     if not args.no_sweep:
         pts = []
         for T in configs.SWEEP_T:
             _, _, us, _, _ = run_gpu(configs.sweep(T), 3, 1)
             pts.append((T, float(np.median(us)) * 1e-3))
+        routed_ms.update(pts)
         x = np.log([p[0] for p in pts])
         y = np.log([p[1] for p in pts])
         line["sweep"] = dict(points_ms={str(T): ms for T, ms in pts},
                              exponent=float(np.polyfit(x, y, 1)[0]))
+    if not args.no_dense:
+        # routed step (index build + route + attention) against dense causal
+        # attention on the same q, k, v, 4K to 64K tokens
+        cmp_t = (*configs.SWEEP_T, 2 * configs.SWEEP_T[-1])
+        pts = {}
+        for T in cmp_t:
+            c = configs.sweep(T)
+            if T not in routed_ms:
+                _, _, us, _, _ = run_gpu(c, 3, 1)
+                routed_ms[T] = float(np.median(us)) * 1e-3
+            dms = time_dense(c)
+            pts[str(T)] = dict(routed_ms=routed_ms[T], dense_ms=dms,
+                               dense_over_routed=dms / routed_ms[T],
+                               dense_mfma_frac=dense_flops(c) / (dms * 1e-3) / 1e12 /
+                               BF16_MFMA_TFLOPS)
+        line["dense_vs_routed"] = pts
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

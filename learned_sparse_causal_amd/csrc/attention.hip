@@ -940,22 +940,48 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
 // dense side of that comparison, on the same rotation pass and tile step as
 // the selected-set kernels.
 
+// Max of a lane's value and those of the lanes 16, 32 and 48 away:
+// the four lanes that hold one query's scores in the MFMA output layout.
+__device__ __forceinline__ float quad_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Largest growth (log2 units) of a row's maximum that is absorbed without
+// rescaling: probabilities stay below 2^8 and the running sums far from
+// overflow; the result does not depend on when rescaling happens beyond
+// rounding.
+constexpr float DENSE_SLACK = 8.0f;
+
 // One wave, NG groups of 16 queries (qf[g]: B fragments of Q^T as in
 // attend64) against 64 keys; each K and V^T fragment read from LDS serves
-// every group.  MASK: keys after a lane's query (qlim[g]) are masked.
-template <int D, bool BF16, bool MASK, int NG>
-__device__ __forceinline__ void attend64_groups(const Frag8<BF16> (&qf)[NG][D / 32],
-                                                const Elem<BF16> *Ks, const Elem<BF16> *Vt,
-                                                int key0, const int (&qlim)[NG],
-                                                f32x4 (&o)[NG][D / 16], float (&m)[NG],
-                                                float (&l)[NG]) {
+// every group.  The running state is kept against a reference maximum m
+// that is only raised when a row's scores exceed it by more than
+// DENSE_SLACK: the score accumulators start at -m, so the logits come out of
+// the MFMA already shifted, and the output is rescaled only on those rare
+// tiles (decided per wave).  The row sums come from the MFMA too: P times an
+// all-ones 16-row block leaves the sum over the tile's keys (of the same
+// rounded P that multiplies V) in every element of l[g].  FIRST: the state is
+// empty and m is set to the tile's row maximum (every row sees key 0 on its
+// first tile).  MASK: keys after a lane's query (qlim[g]) are masked.
+template <int D, bool BF16, bool MASK, bool FIRST, int NG>
+__device__ __forceinline__ void dense_tile(const Frag8<BF16> (&qf)[NG][D / 32],
+                                           const Elem<BF16> *Ks, const Elem<BF16> *Vt, int key0,
+                                           const int (&qlim)[NG], f32x4 (&o)[NG][D / 16],
+                                           float (&m)[NG], f32x4 (&l)[NG]) {
     using T = Tile<D, BF16>;
     const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
     f32x4 st[NG][4];
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < NG; ++g) {
+        const float init = FIRST ? 0.0f : -m[g];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) st[g][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 4; ++mt) st[g][mt] = f32x4{init, init, init, init};
+    }
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
 #pragma unroll
@@ -965,10 +991,10 @@ __device__ __forceinline__ void attend64_groups(const Frag8<BF16> (&qf)[NG][D / 
             for (int g = 0; g < NG; ++g) mma32(st[g][mt], kf, qf[g][c]);
         }
     }
-    Frag8<BF16> pf[NG][2];
+    float mx[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-        float mx = m[g];
+        float x = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -977,30 +1003,45 @@ __device__ __forceinline__ void attend64_groups(const Frag8<BF16> (&qf)[NG][D / 
                     const int key = key0 + mt * 16 + 4 * lg + r;
                     st[g][mt][r] = key <= qlim[g] ? st[g][mt][r] : -INFINITY;
                 }
-                mx = fmaxf(mx, st[g][mt][r]);
+                x = fmaxf(x, st[g][mt][r]);
             }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool none = mx == -INFINITY;   // no key of this row seen yet
-        const float msub = none ? 0.0f : mx;
+        mx[g] = quad_max(x);
+    }
+    if constexpr (FIRST) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            m[g] = mx[g];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) st[g][mt] -= mx[g];
+        }
+    } else {
+        bool grow = false;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) grow = grow || mx[g] > DENSE_SLACK;
+        if (__ballot(grow) != 0ull) {   // raise the reference of every row that grew
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const float up = fmaxf(mx[g], 0.0f);   // a fully masked row has mx = -inf
+                const float alpha = __builtin_amdgcn_exp2f(-up);
+                m[g] += up;
+                l[g] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) o[g][dt] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) st[g][mt] -= up;
+            }
+        }
+    }
+    Frag8<BF16> pf[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
         float p[4][4];
-        float ps = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[mt][r] = __builtin_amdgcn_exp2f(st[g][mt][r] - msub);
-                ps += p[mt][r];
-            }
-        }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m[g] - mx);   // exp2(-inf) = 0
-        l[g] = l[g] * alpha + ps;
-        if (!none) m[g] = mx;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[g][dt] *= alpha;
+            for (int r = 0; r < 4; ++r)
+                p[mt][r] = __builtin_amdgcn_exp2f(st[g][mt][r]);   // exp2(-inf) = 0
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const float pv[8] = {p[2 * c][0], p[2 * c][1], p[2 * c][2], p[2 * c][3],
@@ -1012,13 +1053,77 @@ __device__ __forceinline__ void attend64_groups(const Frag8<BF16> (&qf)[NG][D / 
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-            const Elem<BF16> *vr = Vt + (dt * 16 + lr) * T::VS + 32 * c + 4 * lg;
-            const Frag8<BF16> vf = lds_frag4x2(vr, vr + 16);
+            // bf16 V^T tiles are stored swizzled (VtStagerPacked)
+            const int sw = BF16 ? 8 * dt : 0;
+            const Elem<BF16> *vr = Vt + (dt * 16 + lr) * T::VS;
+            const Frag8<BF16> vf = lds_frag4x2(vr + ((32 * c + 4 * lg) ^ sw),
+                                               vr + ((32 * c + 16 + 4 * lg) ^ sw));
 #pragma unroll
             for (int g = 0; g < NG; ++g) mma32(o[g][dt], vf, pf[g][c]);
         }
+        const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+        const Frag8<BF16> ones = reg_frag8<BF16>(one);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (FIRST && c == 0) l[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            mma32(l[g], ones, pf[g][c]);
+        }
     }
 }
+
+// V^T tile stager for bf16 (256 threads): each task takes 4 consecutive
+// keys x 4 dims (four 8-byte loads) and writes, per dim, the 4 keys as one
+// 8-byte LDS store.  The 4-key granules of dim row r are stored XOR-swizzled
+// by 2 (r / 16), i.e. key column x of row r sits at x ^ (8 (r / 16)): the
+// stores of a half-wave (16 dim chunks x 2 quads, or 32 chunks x 1 quad)
+// then fall on distinct banks, while a fragment read (16 rows of one 16-row
+// block) sees one XOR for all its lanes.
+template <int D>
+struct VtStagerPacked {
+    static constexpr int NC = D / 4;                // 4-dim chunks per key row
+    static constexpr int PER = 16 * NC / 256;       // tasks per thread
+    uint2 v[PER][4];
+    __device__ __forceinline__ void issue(const u16 *src, size_t row0, size_t stride) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int task = threadIdx.x + p * 256;
+            const int c = task % NC, j = task / NC;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[p][i] = *reinterpret_cast<const uint2 *>(src + row0 + (size_t)(4 * j + i) * stride +
+                                                           4 * c);
+        }
+    }
+    __device__ __forceinline__ void commit(u16 *dst) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int task = threadIdx.x + p * 256;
+            const int c = task % NC, j = task / NC;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t x = e < 2 ? v[p][i].x : v[p][i].y;
+                    w[i] = (e & 1) ? x >> 16 : x & 0xFFFFu;
+                }
+                const int row = 4 * c + e;
+                *reinterpret_cast<uint2 *>(dst + row * Tile<D, true>::VS +
+                                           ((4 * j) ^ (8 * (row >> 4)))) =
+                    make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+            }
+        }
+    }
+};
+
+template <int D, bool BF16>
+struct DenseVt {
+    using type = VtStager<D, BF16>;
+};
+template <int D>
+struct DenseVt<D, true> {
+    using type = VtStagerPacked<D>;
+};
 
 constexpr int DENSE_NG = 2;                      // 16-query groups per wave
 constexpr int DENSE_ROWS = 4 * 16 * DENSE_NG;    // queries per workgroup (4 waves)
@@ -1038,7 +1143,7 @@ constexpr size_t dense_lds_bytes() {
 // workgroups of one head sweep its keys from the start at about the same
 // pace and share them in that XCD's L2.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void k_dense(Shape s, const Elem<BF16> *__restrict__ q_rot,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void k_dense(Shape s, const Elem<BF16> *__restrict__ q_rot,
                                                const Elem<BF16> *__restrict__ k_rot,
                                                const Elem<BF16> *__restrict__ v,
                                                Elem<BF16> *__restrict__ out) {
@@ -1068,7 +1173,7 @@ __global__ __launch_bounds__(256) void k_dense(Shape s, const Elem<BF16> *__rest
         qst[gi].issue(q_rot, (((size_t)b * T_ + qlim[gi]) * Hq + h) * D, wave_rows);
     }
     RowStager<D, BF16> kst;
-    VtStager<D, BF16> vst;
+    typename DenseVt<D, BF16>::type vst;
     auto issue_kv = [&](int kt) {
         const int kb0 = kt * 64;
         kst.issue(k_rot, [&](int r, size_t &off) {
@@ -1085,24 +1190,35 @@ __global__ __launch_bounds__(256) void k_dense(Shape s, const Elem<BF16> *__rest
     vst.commit(buf + T::K_ELEMS);
     __syncthreads();
 
-    f32x4 o[NG][D / 16];
-    float m[NG], l[NG];
+    f32x4 o[NG][D / 16], l[NG];
+    float m[NG];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-        m[gi] = -INFINITY;
-        l[gi] = 0.0f;
+        m[gi] = 0.0f;
+        l[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[gi][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int kt = 0; kt < nkt; ++kt) {
+    // key tile 0: every wave with rows takes it first (it holds key 0)
+    if (nkt > 1) issue_kv(1);
+    if (wave_rows) {
+        if (63 > w0) dense_tile<D, BF16, true, true, NG>(qf, buf, buf + T::K_ELEMS, 0, qlim, o, m, l);
+        else dense_tile<D, BF16, false, true, NG>(qf, buf, buf + T::K_ELEMS, 0, qlim, o, m, l);
+    }
+    if (nkt > 1) {
+        kst.commit(buf + BUF);
+        vst.commit(buf + BUF + T::K_ELEMS);
+    }
+    __syncthreads();
+    for (int kt = 1; kt < nkt; ++kt) {
         if (kt + 1 < nkt) issue_kv(kt + 1);    // in flight during this tile's compute
         const E *Ks = buf + (kt & 1) * BUF;
         const int key0 = kt * 64;
         if (wave_rows && key0 <= w0 + 16 * NG - 1) {
             if (key0 + 63 > w0)
-                attend64_groups<D, BF16, true, NG>(qf, Ks, Ks + T::K_ELEMS, key0, qlim, o, m, l);
+                dense_tile<D, BF16, true, false, NG>(qf, Ks, Ks + T::K_ELEMS, key0, qlim, o, m, l);
             else
-                attend64_groups<D, BF16, false, NG>(qf, Ks, Ks + T::K_ELEMS, key0, qlim, o, m, l);
+                dense_tile<D, BF16, false, false, NG>(qf, Ks, Ks + T::K_ELEMS, key0, qlim, o, m, l);
         }
         if (kt + 1 < nkt) {
             E *nb = buf + ((kt + 1) & 1) * BUF;   // last read in the previous tile
@@ -1122,7 +1238,7 @@ __global__ __launch_bounds__(256) void k_dense(Shape s, const Elem<BF16> *__rest
     const int rr = lane >> 2, qq = lane & 3;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-        const float inv = 1.0f / l[gi];
+        const float inv = 1.0f / l[gi][0];
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
             const float x[4] = {o[gi][dt][0] * inv, o[gi][dt][1] * inv, o[gi][dt][2] * inv,
