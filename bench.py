@@ -12,7 +12,7 @@ attention kernel (mono_dense_attention) at 4K-64K tokens, and the CPU oracle
 timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-dense]
-                    [--no-cpu-baseline] [--copy-calibration]
+                    [--dense-sizes 4096,...] [--no-cpu-baseline] [--copy-calibration]
 
 --copy-calibration runs a plain 256 MiB device copy before the steps; hardware
 counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -200,6 +200,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--dense-sizes", default="4096,8192,16384,32768,65536",
+                    help="token counts of the routed-vs-dense comparison")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the routed attention path is built and timed on a "
@@ -259,7 +261,7 @@ def main():
     if not args.no_dense:
         # routed step (index build + route + attention) against dense causal
         # attention on the same q, k, v, 4K to 64K tokens
-        cmp_t = (*configs.SWEEP_T, 2 * configs.SWEEP_T[-1])
+        cmp_t = [int(x) for x in args.dense_sizes.split(",") if x]
         pts = {}
         for T in cmp_t:
             c = configs.sweep(T)

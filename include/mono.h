@@ -176,10 +176,10 @@ mono_status mono_selected_attention(const mono_config *cfg, const void *q, const
                                     void *stream);
 
 /* Dense causal attention, the baseline the routed path is measured against
- * (news page, section "What to Watch": a comparison with dense
- * FlashAttention-style kernels is the decisive systems test; report page,
- * section "Evidence": with every remote block selected the mixer equals
- * dense causal softmax).
+ * (news page, section "The 99.35 Percent Result Does Not Establish Language
+ * Quality": a comparison with optimized FlashAttention-style dense kernels is
+ * necessary; section "What Sparse-Attention Researchers Should Watch Next":
+ * the GPU benchmark must count routing and index costs).
  *   q   [B][T][Hq][d], k, v [B][T][Hkv][d]  dtype, un-rotated q and k
  *   out [B][T][Hq][d] dtype
  * Query t attends to every token s <= t with logits <rot(q_t), rot(k_s)> /

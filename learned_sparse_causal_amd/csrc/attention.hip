@@ -935,10 +935,12 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
 
 // ---------------------------------------------------------------------------
 // Dense causal attention: every query attends to every key at or before it.
-// The news page (section "What to Watch") names the comparison against dense
-// FlashAttention-style kernels as the decisive systems test; this is the
-// dense side of that comparison, on the same rotation pass and tile step as
-// the selected-set kernels.
+// The news page calls a comparison against optimized FlashAttention-style
+// dense kernels necessary (section "The 99.35 Percent Result Does Not
+// Establish Language Quality") and asks for a GPU benchmark that counts the
+// routing and index costs (section "What Sparse-Attention Researchers Should
+// Watch Next"); this is the dense side of that comparison, on the same
+// rotation pass and tile layouts as the selected-set kernels.
 
 // Max of a lane's value and those of the lanes 16, 32 and 48 away:
 // the four lanes that hold one query's scores in the MFMA output layout.
