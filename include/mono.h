@@ -192,6 +192,47 @@ mono_status mono_dense_attention(const mono_config *cfg, const void *q, const vo
                                  const void *v, const float *rope_cos, const float *rope_sin,
                                  void *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Incremental index for decoding (news page, section "Learned Routing Faces
+ * Dense Attention's Reliability Advantage": a deployed decoder updates its
+ * routing structures as new tokens arrive; section "The 99.35 Percent Result
+ * Does Not Establish Language Quality": decoding brings frequent incremental
+ * updates.  Report page, section "Limits": the key/value cache is outside
+ * the mixer contract, so it is the caller's).
+ *   k_cache  [B][T][Hkv][d] dtype  un-rotated keys; T = cfg->seq_len is the
+ *            cache capacity, tokens 0 .. n_tokens-1 of every sequence are valid
+ *   idx      index arrays laid out for cfg (NB = T / block_size blocks)
+ *   n_indexed  blocks whose summary and address idx already holds (0 for an
+ *            empty index)
+ *   n_tokens   valid tokens per sequence, 0 <= n_tokens <= T
+ * Computes the summary and address of blocks n_indexed .. n_tokens/beta - 1
+ * (as mono_build_index does) and rebuilds offsets, entries, load and
+ * overflow over blocks 0 .. n_tokens/beta - 1; entries past the lists are
+ * -1.  Each list keeps its first `capacity` blocks, so the lists equal those
+ * mono_build_index gives for the first n_tokens/beta blocks.  A partial last
+ * block is not indexed.  MONO_ERR_SHAPE if n_tokens > T or n_indexed is
+ * outside 0 .. n_tokens/beta.  No workspace. */
+mono_status mono_decode_index(const mono_config *cfg, const void *k_cache, const float *rope_cos,
+                              const float *rope_sin, const float *codebooks, const mono_index *idx,
+                              int32_t n_indexed, int32_t n_tokens, void *stream);
+
+/* One decode step: route and attend the token at position `pos` of every
+ * sequence (the same reading of the pages as mono_route and
+ * mono_selected_attention, for one query position).
+ *   q        [B][Hq][d] dtype  un-rotated queries of the new token
+ *   k_cache, v_cache [B][T][Hkv][d] dtype  tokens 0 .. pos valid (the new
+ *            token's key and value already written at pos)
+ *   idx      an index covering at least blocks 0 .. pos/beta - n_local (from
+ *            mono_decode_index or mono_build_index over the same layout)
+ *   sel      [B][Hq][R] int32  output: selected remote blocks, ascending, -1 padded
+ *   out      [B][Hq][d] dtype  output: attention of the new token
+ * The selection and the output equal what mono_route and
+ * mono_selected_attention give row pos of the sequence.  MONO_ERR_SHAPE if
+ * pos is outside 0 .. T-1.  No workspace. */
+mono_status mono_decode_step(const mono_config *cfg, const void *q, const void *k_cache,
+                             const void *v_cache, const float *rope_cos, const float *rope_sin,
+                             const float *codebooks, const mono_index *idx, int32_t pos,
+                             int32_t *sel, void *out, void *stream);
+
 /* The whole mixer (report page, "Mixer" and Figure 1): stateless, normalized
  * stream in, attention delta of the same shape out.
  *   x      [B][T][W] dtype

@@ -59,12 +59,15 @@ def load_library(path=LIB_PATH):
     lib.mono_route.argtypes = [cfgp, P, P, P, P, idxp, P, P, S, P]
     lib.mono_selected_attention.argtypes = [cfgp, P, P, P, P, P, P, P, P, S, P]
     lib.mono_dense_attention.argtypes = [cfgp, P, P, P, P, P, P, P, S, P]
+    lib.mono_decode_index.argtypes = [cfgp, P, P, P, P, idxp, ctypes.c_int32, ctypes.c_int32, P]
+    lib.mono_decode_step.argtypes = [cfgp, P, P, P, P, P, P, idxp, ctypes.c_int32, P, P, P]
     lib.mono_mixer_forward.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, S, P]
     lib.mono_mixer_layout.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
     lib.mono_status_string.argtypes = [I]
     lib.mono_status_string.restype = ctypes.c_char_p
     for f in ("mono_rope_table", "mono_build_index", "mono_route", "mono_selected_attention",
-              "mono_dense_attention", "mono_mixer_forward", "mono_mixer_layout"):
+              "mono_dense_attention", "mono_decode_index", "mono_decode_step",
+              "mono_mixer_forward", "mono_mixer_layout"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -235,6 +238,46 @@ def dense_attention(cfg, q, k, v, rope_cos, rope_sin, out=None, ws=None):
                                                ws.data_ptr() if ws is not None else None,
                                                nws, _stream()))
     return out
+
+
+def decode_index(cfg, k_cache, rope_cos, rope_sin, codebooks, index, n_indexed, n_tokens):
+    """mono_decode_index: index blocks n_indexed .. n_tokens // beta - 1 of the
+    cache and rebuild the lists over the indexed prefix; returns the index."""
+    torch = _torch()
+    c = make_config(cfg)
+    st = _index_struct(cfg, index)
+    args = (_need(k_cache, (cfg.B, cfg.T, cfg.Hkv, cfg.d), _act_dtype(cfg), "k_cache"),
+            _need(rope_cos, (cfg.T, cfg.d // 2), torch.float32, "rope_cos"),
+            _need(rope_sin, (cfg.T, cfg.d // 2), torch.float32, "rope_sin"),
+            _need(codebooks, (cfg.Hkv, cfg.P, cfg.K, cfg.d // cfg.P), torch.float32, "codebooks"))
+    _check(load_library().mono_decode_index(ctypes.byref(c), *args, ctypes.byref(st),
+                                            int(n_indexed), int(n_tokens), _stream()))
+    return index
+
+
+def decode_step(cfg, q, k_cache, v_cache, rope_cos, rope_sin, codebooks, index, pos, sel=None,
+                out=None):
+    """mono_decode_step: returns (sel [B, Hq, R] int32, out [B, Hq, d]) for the
+    token at position pos."""
+    torch = _torch()
+    c = make_config(cfg)
+    dt = _act_dtype(cfg)
+    st = _index_struct(cfg, index)
+    if sel is None:
+        sel = torch.empty((cfg.B, cfg.Hq, cfg.R), dtype=torch.int32, device="cuda")
+    if out is None:
+        out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=dt, device="cuda")
+    args = (_need(q, (cfg.B, cfg.Hq, cfg.d), dt, "q"),
+            _need(k_cache, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "k_cache"),
+            _need(v_cache, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "v_cache"),
+            _need(rope_cos, (cfg.T, cfg.d // 2), torch.float32, "rope_cos"),
+            _need(rope_sin, (cfg.T, cfg.d // 2), torch.float32, "rope_sin"),
+            _need(codebooks, (cfg.Hkv, cfg.P, cfg.K, cfg.d // cfg.P), torch.float32, "codebooks"))
+    _check(load_library().mono_decode_step(ctypes.byref(c), *args, ctypes.byref(st), int(pos),
+                                           _need(sel, (cfg.B, cfg.Hq, cfg.R), torch.int32, "sel"),
+                                           _need(out, (cfg.B, cfg.Hq, cfg.d), dt, "out"),
+                                           _stream()))
+    return sel, out
 
 
 def mixer_layout(cfg):

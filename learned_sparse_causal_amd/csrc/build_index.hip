@@ -55,7 +55,7 @@ size_t block_address_lds(const Shape &s, int ct) {
 // component (lowest code on ties) and writes the address.  MAXP bounds the
 // pairs per thread (Hkv d / 2 <= 256 MAXP).
 template <int D, int P, bool BF16, int MAXP>
-__global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT,
+__global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, int n0,
                                                               const void *__restrict__ k,
                                                               const float *__restrict__ cos_t,
                                                               const float *__restrict__ sin_t,
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT,
     float *sc = kb + Hkv * D;                                   // [Hkv][PK]
 
     const int tid = threadIdx.x;
-    const int n = blockIdx.x, b = blockIdx.y;
+    const int n = n0 + blockIdx.x, b = blockIdx.y;
     const int t0 = n * s.beta;
     const int npairs = Hkv * H;
     const int vecs = CT * rowE * ES / 16;                       // 16-byte vectors per chunk
@@ -204,7 +204,9 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT,
 
 constexpr int PL_THREADS = 256;
 
-__global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s,
+// nbu: blocks 0 .. nbu-1 are indexed (NB for a whole sequence); arrays keep
+// their NB strides.
+__global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
                                                               const int32_t *__restrict__ addr,
                                                               int32_t *__restrict__ offsets,
                                                               int32_t *__restrict__ entries,
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s,
     const int tid = threadIdx.x;
     for (int a = tid; a < A; a += PL_THREADS) { hist[a] = 0; run[a] = 0; }
     __syncthreads();
-    for (int n = tid; n < NB; n += PL_THREADS) atomicAdd(&hist[ad[n]], 1);
+    for (int n = tid; n < nbu; n += PL_THREADS) atomicAdd(&hist[ad[n]], 1);
     __syncthreads();
 
     // exclusive scan of min(load, cap): each thread owns a contiguous chunk
@@ -283,9 +285,9 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s,
         int nbits = 0;
         while ((1 << nbits) < A) ++nbits;
         const uint64_t lt = (1ull << tid) - 1ull;
-        for (int c0 = 0; c0 < NB; c0 += WAVE) {
+        for (int c0 = 0; c0 < nbu; c0 += WAVE) {
             const int n = c0 + tid;
-            const bool in = n < NB;
+            const bool in = n < nbu;
             const int a = in ? ad[n] : 0;
             uint64_t m = __ballot(in);
             for (int bit = 0; bit < nbits; ++bit) {
@@ -305,9 +307,9 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s,
 
 // ---------------------------------------------------------------- launchers
 template <int D, int P, bool BF16, int MAXP>
-hipError_t launch_ba_t(const Shape &s, int ct, size_t lds, const void *k, const float *cos_t,
-                       const float *sin_t, const float *cb, float *kbar, int32_t *addr,
-                       hipStream_t st) {
+hipError_t launch_ba_t(const Shape &s, int n0, int n1, int ct, size_t lds, const void *k,
+                       const float *cos_t, const float *sin_t, const float *cb, float *kbar,
+                       int32_t *addr, hipStream_t st) {
     auto *fn = k_block_address<D, P, BF16, MAXP>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -315,44 +317,62 @@ hipError_t launch_ba_t(const Shape &s, int ct, size_t lds, const void *k, const 
                                                  (int)lds);
         if (e != hipSuccess) return e;
     }
-    fn<<<dim3((unsigned)s.NB, (unsigned)s.B), BA_THREADS, lds, st>>>(s, ct, k, cos_t, sin_t, cb,
-                                                                     kbar, addr);
+    fn<<<dim3((unsigned)(n1 - n0), (unsigned)s.B), BA_THREADS, lds, st>>>(s, ct, n0, k, cos_t,
+                                                                          sin_t, cb, kbar, addr);
     return hipGetLastError();
 }
 
 template <int D, bool BF16>
-hipError_t launch_ba(const Shape &s, const void *k, const float *cos_t, const float *sin_t,
-                     const float *cb, float *kbar, int32_t *addr, hipStream_t st) {
+hipError_t launch_ba(const Shape &s, int n0, int n1, const void *k, const float *cos_t,
+                     const float *sin_t, const float *cb, float *kbar, int32_t *addr,
+                     hipStream_t st) {
     const int ct = block_chunk_tokens(s);
     const size_t lds = block_address_lds(s, ct);
     const bool small = s.Hkv * (D / 2) <= 2 * BA_THREADS;
+#define MONO_BA_ARGS s, n0, n1, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st
     if (s.P == 1)
-        return small ? launch_ba_t<D, 1, BF16, 2>(s, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st)
-                     : launch_ba_t<D, 1, BF16, 8>(s, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st);
-    return small ? launch_ba_t<D, 2, BF16, 2>(s, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st)
-                 : launch_ba_t<D, 2, BF16, 8>(s, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st);
+        return small ? launch_ba_t<D, 1, BF16, 2>(MONO_BA_ARGS)
+                     : launch_ba_t<D, 1, BF16, 8>(MONO_BA_ARGS);
+    return small ? launch_ba_t<D, 2, BF16, 2>(MONO_BA_ARGS)
+                 : launch_ba_t<D, 2, BF16, 8>(MONO_BA_ARGS);
+#undef MONO_BA_ARGS
 }
 
 }  // namespace
 
+// Summaries and addresses of blocks n0 .. n1-1 of every sequence.
+hipError_t launch_block_address_range(const Shape &s, int n0, int n1, const void *k,
+                                      const float *cos_t, const float *sin_t, const float *cb,
+                                      float *kbar, int32_t *addr, hipStream_t st) {
+    if (n1 <= n0) return hipSuccess;
+    const bool bf = s.dtype == 1;
+    if (s.d == 64)
+        return bf ? launch_ba<64, true>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, st)
+                  : launch_ba<64, false>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, st);
+    return bf ? launch_ba<128, true>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, st)
+              : launch_ba<128, false>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, st);
+}
+
 hipError_t launch_block_address(const Shape &s, const void *k, const float *cos_t,
                                 const float *sin_t, const float *cb, float *kbar, int32_t *addr,
                                 hipStream_t st) {
-    const bool bf = s.dtype == 1;
-    if (s.d == 64)
-        return bf ? launch_ba<64, true>(s, k, cos_t, sin_t, cb, kbar, addr, st)
-                  : launch_ba<64, false>(s, k, cos_t, sin_t, cb, kbar, addr, st);
-    return bf ? launch_ba<128, true>(s, k, cos_t, sin_t, cb, kbar, addr, st)
-              : launch_ba<128, false>(s, k, cos_t, sin_t, cb, kbar, addr, st);
+    return launch_block_address_range(s, 0, s.NB, k, cos_t, sin_t, cb, kbar, addr, st);
+}
+
+// Lists of blocks 0 .. nbu-1 (the indexed prefix of every sequence).
+hipError_t launch_posting_lists_prefix(const Shape &s, int nbu, const int32_t *addr,
+                                       int32_t *offsets, int32_t *entries, int32_t *load,
+                                       int32_t *overflow, hipStream_t st) {
+    const size_t lds = (size_t)(3 * s.A + 1) * sizeof(int32_t);
+    k_posting_lists<<<dim3(s.B * s.Hkv), PL_THREADS, lds, st>>>(s, nbu, addr, offsets, entries,
+                                                                 load, overflow);
+    return hipGetLastError();
 }
 
 hipError_t launch_posting_lists(const Shape &s, const int32_t *addr, int32_t *offsets,
                                 int32_t *entries, int32_t *load, int32_t *overflow,
                                 hipStream_t st) {
-    const size_t lds = (size_t)(3 * s.A + 1) * sizeof(int32_t);
-    k_posting_lists<<<dim3(s.B * s.Hkv), PL_THREADS, lds, st>>>(s, addr, offsets, entries, load,
-                                                                 overflow);
-    return hipGetLastError();
+    return launch_posting_lists_prefix(s, s.NB, addr, offsets, entries, load, overflow, st);
 }
 
 // Totals of an index: stats[0] = sum of overflow, stats[1] = maximum load.

@@ -25,6 +25,16 @@ size_t attention_ws_layout(const Shape &s, size_t *off);
 hipError_t launch_attention(const Shape &s, const void *q, const void *k, const void *v,
                             const float *cos_t, const float *sin_t, const int32_t *sel, void *out,
                             void *ws, hipStream_t st);
+hipError_t launch_block_address_range(const Shape &s, int n0, int n1, const void *k,
+                                      const float *cos_t, const float *sin_t, const float *cb,
+                                      float *kbar, int32_t *addr, hipStream_t st);
+hipError_t launch_posting_lists_prefix(const Shape &s, int nbu, const int32_t *addr,
+                                       int32_t *offsets, int32_t *entries, int32_t *load,
+                                       int32_t *overflow, hipStream_t st);
+hipError_t launch_decode(const Shape &s, int pos, const void *q, const void *kc, const void *vc,
+                         const float *cos_t, const float *sin_t, const float *cb,
+                         const float *kbar, const int32_t *offsets, const int32_t *entries,
+                         int32_t *sel, void *out, hipStream_t st);
 size_t dense_ws_layout(const Shape &s, size_t *off);
 hipError_t launch_dense(const Shape &s, const void *q, const void *k, const void *v,
                         const float *cos_t, const float *sin_t, void *out, void *ws,
@@ -212,6 +222,40 @@ mono_status mono_dense_attention(const mono_config *cfg, const void *q, const vo
     if (ws_bytes < dense_ws_layout(s, off)) return MONO_ERR_WORKSPACE;
     return hip_status(launch_dense(s, q, k, v, rope_cos, rope_sin, out, ws,
                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+mono_status mono_decode_index(const mono_config *cfg, const void *k_cache, const float *rope_cos,
+                              const float *rope_sin, const float *codebooks, const mono_index *idx,
+                              int32_t n_indexed, int32_t n_tokens, void *stream) {
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!k_cache || !rope_cos || !rope_sin || !codebooks || !index_ok(idx)) return MONO_ERR_NULL;
+    if (n_tokens < 0 || n_tokens > s.T) return MONO_ERR_SHAPE;
+    const int nb = n_tokens / s.beta;
+    if (n_indexed < 0 || n_indexed > nb) return MONO_ERR_SHAPE;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (launch_block_address_range(s, n_indexed, nb, k_cache, rope_cos, rope_sin, codebooks,
+                                   idx->kbar, idx->addr, hs) != hipSuccess)
+        return MONO_ERR_HIP;
+    return hip_status(launch_posting_lists_prefix(s, nb, idx->addr, idx->offsets, idx->entries,
+                                                  idx->load, idx->overflow, hs));
+}
+
+mono_status mono_decode_step(const mono_config *cfg, const void *q, const void *k_cache,
+                             const void *v_cache, const float *rope_cos, const float *rope_sin,
+                             const float *codebooks, const mono_index *idx, int32_t pos,
+                             int32_t *sel, void *out, void *stream) {
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!q || !k_cache || !v_cache || !rope_cos || !rope_sin || !codebooks || !index_ok(idx) ||
+        !sel || !out)
+        return MONO_ERR_NULL;
+    if (pos < 0 || pos >= s.T) return MONO_ERR_SHAPE;
+    return hip_status(launch_decode(s, pos, q, k_cache, v_cache, rope_cos, rope_sin, codebooks,
+                                    idx->kbar, idx->offsets, idx->entries, sel, out,
+                                    reinterpret_cast<hipStream_t>(stream)));
 }
 
 mono_status mono_mixer_layout(const mono_config *cfg, size_t *offsets_out) {

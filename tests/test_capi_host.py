@@ -113,3 +113,26 @@ def test_attention_and_mixer_argument_errors(lib):
     assert lib.mono_dense_attention(ctypes.byref(c), one, one, one, one, one, one, one, need - 1,
                                     None) == 4
     assert lib.mono_status_string(4) == b"workspace too small"
+
+
+def test_decode_argument_errors(lib):
+    cfg = configs.TINY
+    c = binding.make_config(cfg)
+    one = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    idx = binding.MonoIndex(*(256,) * 6)
+    # token count beyond the cache, indexed blocks beyond the token count
+    assert lib.mono_decode_index(ctypes.byref(c), one, one, one, one, ctypes.byref(idx), 0,
+                                 cfg.T + 1, None) == 2
+    assert lib.mono_decode_index(ctypes.byref(c), one, one, one, one, ctypes.byref(idx), 3,
+                                 2 * cfg.beta, None) == 2
+    assert lib.mono_decode_index(ctypes.byref(c), one, one, one, one, ctypes.byref(idx), -1,
+                                 2 * cfg.beta, None) == 2
+    assert lib.mono_decode_index(ctypes.byref(c), None, one, one, one, ctypes.byref(idx), 0,
+                                 cfg.T, None) == 1
+    # position outside the cache, missing outputs
+    assert lib.mono_decode_step(ctypes.byref(c), one, one, one, one, one, one, ctypes.byref(idx),
+                                cfg.T, one, one, None) == 2
+    assert lib.mono_decode_step(ctypes.byref(c), one, one, one, one, one, one, ctypes.byref(idx),
+                                -1, one, one, None) == 2
+    assert lib.mono_decode_step(ctypes.byref(c), one, one, one, one, one, one, ctypes.byref(idx),
+                                0, None, one, None) == 1
