@@ -8,11 +8,13 @@ capacity 64, 4 probes, R = 2 remote + 2 local blocks, bf16).  Prints one JSON
 line: tokens/s, the dominant kernel's roofline (its duration taken from HIP
 events recorded around its launches inside the timed steps), the per-stage
 floors, the 4K-32K sweep exponent, the routed step against the dense causal
-attention kernel (mono_dense_attention) at 4K-64K tokens, and the CPU oracle
-timed on the host cores.
+attention kernel (mono_dense_attention) at 4K-64K tokens, one decode step
+(mono_decode_step) and index update (mono_decode_index) on the batch-8
+64K-token cache, and the CPU oracle timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-dense]
-                    [--dense-sizes 4096,...] [--no-cpu-baseline] [--copy-calibration]
+                    [--dense-sizes 4096,...] [--no-decode] [--no-cpu-baseline]
+                    [--copy-calibration]
 
 --copy-calibration runs a plain 256 MiB device copy before the steps; hardware
 counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -145,6 +147,62 @@ def time_dense(cfg, reps=3, warmup=1):
     return float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
 
 
+def run_decode(cfg, steps=20, warmup=3):
+    """Decode on a full cache of cfg.T tokens: mono_decode_step for the last
+    position (route + attend of B x Hq new-token queries) and mono_decode_index
+    re-indexing the last block (its summary and address, then the list
+    rebuild), each timed with HIP events on the launch stream; medians in us.
+    Algorithmic bytes of a step: per (batch, kv-head) the key and value rows
+    of the union of its heads' selected and local tokens, plus q, out and sel."""
+    import torch
+    from learned_sparse_causal_amd import binding, synth
+    d = synth.qkv_device(cfg)
+    cos, sin = binding.device_rope(cfg)
+    cb = torch.from_numpy(d["codebooks"]).cuda()
+    idx = binding.build_index(cfg, d["k"], cos, sin, cb)
+    pos = cfg.T - 1
+    q = d["q"][:, pos].contiguous()
+    sel = torch.empty((cfg.B, cfg.Hq, cfg.R), dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=q.dtype, device="cuda")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in ev:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+
+    step_us = timed(lambda: binding.decode_step(cfg, q, d["k"], d["v"], cos, sin, cb, idx, pos,
+                                                sel, out))
+    index_us = timed(lambda: binding.decode_index(cfg, d["k"], cos, sin, cb, idx, cfg.NB - 1,
+                                                  cfg.T))
+    es = 2 if cfg.dtype == "bf16" else 4
+    s_np = sel.cpu().numpy()
+    qb = pos // cfg.beta
+    local = set(range(max(0, qb - cfg.L + 1), qb + 1))
+    tokens = 0
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            blocks = set(local)
+            for h in range(g * cfg.G, (g + 1) * cfg.G):
+                blocks.update(int(x) for x in s_np[b, h] if x >= 0)
+            tokens += sum(min(cfg.beta, pos + 1 - n * cfg.beta) for n in blocks)
+    step_bytes = tokens * 2 * cfg.d * es + cfg.B * cfg.Hq * (2 * cfg.d * es + 4 * cfg.R)
+    return dict(workload=cfg.name, B=cfg.B, cache_tokens=cfg.T, position=pos,
+                step_us=step_us, tokens_per_s=cfg.B / (step_us * 1e-6),
+                index_update_us=index_us,
+                roofline=dict(bound="hbm", achieved=step_bytes / (step_us * 1e-6) / 1e9,
+                              peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=step_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                              bytes=step_bytes),
+                dense_kv_floor_us=cfg.B * cfg.Hkv * cfg.T * 2 * cfg.d * es / (HBM_PEAK_GBS * 1e9)
+                * 1e6)
+
+
 def dense_flops(cfg):
     """Causal dense attention: 2 d flops for q.k and 2 d for p.v per (query, key <= query)."""
     return 4.0 * cfg.d * cfg.B * cfg.Hq * cfg.T * (cfg.T + 1) / 2
@@ -200,6 +258,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--dense-sizes", default="4096,8192,16384,32768,65536",
                     help="token counts of the routed-vs-dense comparison")
     args = ap.parse_args()
@@ -274,6 +333,8 @@ def main():
                                dense_mfma_frac=dense_flops(c) / (dms * 1e-3) / 1e12 /
                                BF16_MFMA_TFLOPS)
         line["dense_vs_routed"] = pts
+    if not args.no_decode:
+        line["decode"] = run_decode(configs.LARGE)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

@@ -48,6 +48,9 @@ def load_library(path=LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise OSError("libmono.so is not built (run `python -m learned_sparse_causal_amd.build`)")
+    # torch first: the library then binds to the HIP runtime torch loaded, so
+    # its kernels and torch's memory and streams belong to one runtime
+    _torch()
     lib = ctypes.CDLL(path)
     P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     cfgp = ctypes.POINTER(MonoConfig)

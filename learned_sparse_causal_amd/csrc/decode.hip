@@ -13,8 +13,9 @@
 // whole-sequence build does), and each new query takes the route and the
 // attention that the whole-sequence path gives its position.
 //
-// k_decode_route: one wave per route.  The rotated query and its code
-//   scores go to LDS (fp32, fused multiply-add chains in dimension order,
+// k_decode_route: one wave per route.  The (batch, kv-head) list offsets and
+//   entries are staged in LDS once.  The rotated query and its code scores go
+//   to LDS (fp32, fused multiply-add chains in dimension order,
 //   rotation products rounded before the add: the same arithmetic as the
 //   whole-sequence router, so the decisions are bit-identical); address sums
 //   are kept per lane.  Addresses are visited in (sum desc, address asc)
@@ -26,9 +27,11 @@
 //   in ascending order.
 // k_decode_attend: one workgroup per (batch, q-head).  The local blocks and
 //   the valid, first-occurrence selected blocks are split in 64-key items
-//   over four waves; each lane scores one key (rotated in fp32 from the
-//   cache), each wave keeps an online softmax, and the four states are
+//   over eight waves; four lanes score one key (rotated in fp32 from the
+//   cache), each wave keeps an online softmax and accumulates P V with the
+//   64 value rows of an item loaded back to back, and the eight states are
 //   merged through LDS.
+#include <algorithm>
 #include <climits>
 
 #include "common.hpp"
@@ -37,47 +40,113 @@ namespace {
 
 constexpr int DR_THREADS = WAVE;   // one wave per route
 
-// (score, id) is ordered before (score', id') when score > score', or
-// scores are equal and id < id'.
-__device__ __forceinline__ bool ahead(float s, int i, float s2, int i2) {
-    return s > s2 || (s == s2 && i < i2);
+// (score, id) as one unsigned 64-bit key: (score, id) is ordered before
+// (score', id') -- score > score', or equal scores and id < id' -- exactly
+// when its key is larger.  The score's bits are mapped to an order-preserving
+// unsigned integer (-0 taken as +0, as the float comparison does).
+__device__ __forceinline__ uint64_t order_key(float sc, int id) {
+    const uint32_t u = __float_as_uint(sc + 0.0f);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
 }
 
-// Wave arg-max of (score, id) in the order above; every lane gets the result.
-__device__ __forceinline__ void wave_best(float &s, int &i) {
+__device__ __forceinline__ int key_id(uint64_t k) {
+    return (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+__device__ __forceinline__ uint64_t key_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_key(uint64_t k) {
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t swap_max(uint64_t k, bool half32) {
+    const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+    const auto l2 = half32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                           : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h2 = half32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                           : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const uint64_t a = ((uint64_t)h2[0] << 32) | l2[0];
+    const uint64_t b = ((uint64_t)h2[1] << 32) | l2[1];
+    return key_max(a, b);
+}
+
+// Largest key of the wave, in every lane: lane pairs within quads, then the
+// half-row and row mirrors, then the gfx950 row and half-wave swaps (no LDS).
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+    k = key_max(k, dpp_key<0xB1>(k));    // quad_perm 1,0,3,2
+    k = key_max(k, dpp_key<0x4E>(k));    // quad_perm 2,3,0,1
+    k = key_max(k, dpp_key<0x141>(k));   // row_half_mirror
+    k = key_max(k, dpp_key<0x140>(k));   // row_mirror
+    k = swap_max(k, false);
+    return swap_max(k, true);
+}
+
+size_t decode_route_lds(const Shape &s) {
+    // q_rot, code scores, address sums, list offsets, entries, pool ids, pool
+    // scores, extension addresses
+    return (size_t)(s.d + s.P * s.K + s.A + (s.A + 1) + s.NB + 2 * s.NB + std::min(s.A, s.NB)) * 4;
+}
+
+// fp32 fused multiply-add chain over n = N elements in index order, with the
+// b operand read from global memory (all loads issued up front).
+template <int N>
+__device__ __forceinline__ float chain_lds_global(const float *a, const float *__restrict__ bg) {
+    float acc = 0.0f;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float s2 = __shfl_xor(s, o);
-        const int i2 = __shfl_xor(i, o);
-        if (ahead(s2, i2, s, i)) {
-            s = s2;
-            i = i2;
+    for (int j = 0; j < N; j += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(bg + j);
+        acc = fmaf(a[j], v.x, acc);
+        acc = fmaf(a[j + 1], v.y, acc);
+        acc = fmaf(a[j + 2], v.z, acc);
+        acc = fmaf(a[j + 3], v.w, acc);
+    }
+    return acc;
+}
+
+// Stage n ints from global to LDS, eight loads in flight per lane.
+__device__ __forceinline__ void stage_ints(int *dst, const int32_t *__restrict__ src, int n,
+                                           int lane) {
+    for (int b0 = 0; b0 < n; b0 += 8 * WAVE) {
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = b0 + k * WAVE + lane;
+            v[k] = i < n ? src[i] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = b0 + k * WAVE + lane;
+            if (i < n) dst[i] = v[k];
         }
     }
 }
 
-size_t decode_route_lds(const Shape &s) {
-    return (size_t)(s.d + s.P * s.K + s.A + 2 * s.NB) * 4;
-}
-
-template <int D, bool BF16>
+template <int D, int P, bool BF16>
 __global__ __launch_bounds__(DR_THREADS) void k_decode_route(
     Shape s, int pos, const void *__restrict__ q, const float *__restrict__ cos_t,
     const float *__restrict__ sin_t, const float *__restrict__ cb, const float *__restrict__ kbar,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ entries,
     int32_t *__restrict__ sel) {
-    constexpr int H = D / 2;
+    constexpr int H = D / 2, DS = D / P;
     extern __shared__ __align__(16) float dr_lds[];
-    float *qr = dr_lds;                          // [D] rotated query
-    float *sc = qr + D;                          // [P K] code scores
-    float *sig = sc + s.P * s.K;                 // [A] address sums
-    int *pool_n = reinterpret_cast<int *>(sig + s.A);     // [NB]
-    float *pool_r = reinterpret_cast<float *>(pool_n + s.NB);   // [NB]
+    const int R = s.R, K = s.K, A = s.A, NB = s.NB;
+    float *qr = dr_lds;                                  // [D] rotated query
+    float *sc = qr + D;                                  // [P K] code scores
+    float *sig = sc + P * K;                             // [A] address sums
+    int *off = reinterpret_cast<int *>(sig + A);         // [A + 1] list offsets
+    int *ent = off + A + 1;                              // [NB] list entries
+    int *pool_n = ent + NB;                              // [NB] pooled blocks
+    float *pool_r = reinterpret_cast<float *>(pool_n + NB);   // [NB] their rerank scores
+    int *cand = reinterpret_cast<int *>(pool_r + NB);    // [min(A, NB)] extension addresses
 
-    const int route = blockIdx.x;                // b * Hq + h
+    const int route = blockIdx.x;                        // b * Hq + h
     const int b = route / s.Hq, h = route % s.Hq, g = h / s.G;
     const int lane = threadIdx.x;
-    const int R = s.R, P = s.P, K = s.K, A = s.A, ds = s.ds;
+    const uint64_t lanemask = (1ull << lane) - 1ull;
     int32_t *out = sel + (size_t)route * R;
     const int qb = pos / s.beta;
     const int E = max(0, qb - s.L + 1);
@@ -85,6 +154,10 @@ __global__ __launch_bounds__(DR_THREADS) void k_decode_route(
         for (int r = lane; r < R; r += WAVE) out[r] = r < E ? r : -1;
         return;
     }
+    const size_t u = (size_t)b * s.Hkv + g;
+    // the (batch, kv-head) lists, staged once
+    stage_ints(off, offsets + u * (A + 1), A + 1, lane);
+    stage_ints(ent, entries + u * NB, NB, lane);
     // rotate (fp32, products rounded before the add)
     const size_t qoff = (size_t)route * D;
     for (int i = lane; i < H; i += WAVE) {
@@ -99,95 +172,98 @@ __global__ __launch_bounds__(DR_THREADS) void k_decode_route(
     // code scores: fma chains in dimension order
     for (int x = lane; x < P * K; x += WAVE) {
         const int p = x / K;
-        const float *crow = cb + ((size_t)g * P + p) * K * ds + (size_t)(x % K) * ds;
-        const float *qp = qr + p * ds;
-        float acc = 0.0f;
-        for (int j = 0; j < ds; ++j) acc = fmaf(qp[j], crow[j], acc);
-        sc[x] = acc;
+        sc[x] = chain_lds_global<DS>(qr + p * DS, cb + (((size_t)g * P + p) * K + x % K) * DS);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     // address sums, component 0 first (mixed radix, component 0 most significant)
-    for (int a = lane; a < A; a += WAVE) {
-        float v;
-        if (P == 1) {
-            v = sc[a];
-        } else {
-            v = sc[a / K] + sc[K + a % K];
-        }
-        sig[a] = v;
-    }
+    for (int a = lane; a < A; a += WAVE) sig[a] = P == 1 ? sc[a] : sc[a / K] + sc[K + a % K];
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
 
-    const size_t u = (size_t)b * s.Hkv + g;
-    const int32_t *off = offsets + u * (A + 1);
-    const int32_t *ent = entries + u * s.NB;
     const int last = qb - s.L;
-    float s_last = INFINITY;
-    int a_last = -1;
     int npool = 0;
-    for (int probed = 0; probed < A;) {
-        // next address in (sum desc, address asc) order after (s_last, a_last)
-        float bs = -INFINITY;
-        int ba = INT_MAX;
-        for (int a = lane; a < A; a += WAVE) {
-            const float v = sig[a];
-            if (ahead(s_last, a_last, v, a) && ahead(v, a, bs, ba)) {
-                bs = v;
-                ba = a;
-            }
-        }
-        wave_best(bs, ba);
-        if (ba == INT_MAX) break;   // no address left (only with non-finite sums)
-        s_last = bs;
-        a_last = ba;
-        ++probed;
-        // eligible prefix of the list (ascending block ids)
-        const int e0 = off[ba], e1 = off[ba + 1];
+    // the eligible prefix of list a joins the pool
+    auto take = [&](int a) {
+        const int e0 = off[a], e1 = off[a + 1];
         for (int e = e0; e < e1; e += WAVE) {
             const int n = e + lane < e1 ? ent[e + lane] : INT_MAX;
             const bool ok = n <= last;
             const uint64_t m = __ballot(ok);
-            const int slot = npool + __popcll(m & ((1ull << lane) - 1ull));
-            if (ok && slot < s.NB) pool_n[slot] = n;   // a valid index holds <= NB blocks
-            npool = min(s.NB, npool + __popcll(m));
+            const int slot = npool + __popcll(m & lanemask);
+            if (ok && slot < NB) pool_n[slot] = n;   // a valid index holds <= NB blocks
+            npool = min(NB, npool + __popcll(m));
             if (m != ~0ull) break;   // a later block ends the prefix
         }
-        if (probed >= s.npr && npool >= R) break;
+    };
+    // The walk over addresses in (sum desc, address asc) order stops at the
+    // first address at which at least n_probes were visited and R blocks
+    // pooled.  Phase 1 visits the n_probes best addresses; after them only
+    // addresses whose list has an eligible block can change the pool or end
+    // the walk, so phase 2 walks those alone (at most R more rounds).
+    uint64_t prev = ~0ull;                               // key of the last visited address
+    const int np1 = min(A, s.npr);
+    for (int r = 0; r < np1; ++r) {
+        uint64_t best = 0;
+        for (int a = lane; a < A; a += WAVE) {
+            const uint64_t k = order_key(sig[a], a);
+            if (k < prev) best = key_max(best, k);
+        }
+        best = wave_max_key(best);
+        prev = best;
+        take(key_id(best));
+    }
+    if (npool < R && np1 < A) {
+        // addresses after the last visited one whose list starts with an eligible block
+        int ncand = 0;
+        for (int a0 = 0; a0 < A; a0 += WAVE) {
+            const int a = a0 + lane;
+            bool ok = false;
+            if (a < A) {
+                const int e0 = off[a];
+                ok = e0 < off[a + 1] && ent[e0] <= last && order_key(sig[a], a) < prev;
+            }
+            const uint64_t m = __ballot(ok);
+            if (ok) cand[ncand + __popcll(m & lanemask)] = a;
+            ncand += __popcll(m);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        while (npool < R) {
+            uint64_t best = 0;
+            for (int x = lane; x < ncand; x += WAVE) {
+                const int a = cand[x];
+                const uint64_t k = order_key(sig[a], a);
+                if (k < prev) best = key_max(best, k);
+            }
+            best = wave_max_key(best);
+            if (best == 0) break;                        // every list taken
+            prev = best;
+            take(key_id(best));
+        }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     // rerank: fma chain over every dimension of q_rot . kbar_n
-    const float *kb = kbar + u * (size_t)s.NB * D;
-    for (int x = lane; x < npool; x += WAVE) {
-        const float *row = kb + (size_t)pool_n[x] * D;
-        float acc = 0.0f;
-        for (int j = 0; j < D; ++j) acc = fmaf(qr[j], row[j], acc);
-        pool_r[x] = acc;
-    }
+    const float *kb = kbar + u * (size_t)NB * D;
+    for (int x = lane; x < npool; x += WAVE)
+        pool_r[x] = chain_lds_global<D>(qr, kb + (size_t)pool_n[x] * D);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     // the R best in (score desc, block asc) order; lane r keeps pick r
+    // (R <= 16 whenever the search runs)
     const int nsel = min(R, npool);
-    float r_last = INFINITY;
-    int n_last = -1;
+    uint64_t pprev = ~0ull;
     int mine = -1;
     for (int r = 0; r < nsel; ++r) {
-        float bs = -INFINITY;
-        int bn = INT_MAX;
+        uint64_t best = 0;
         for (int x = lane; x < npool; x += WAVE) {
-            const float v = pool_r[x];
-            const int n = pool_n[x];
-            if (ahead(r_last, n_last, v, n) && ahead(v, n, bs, bn)) {
-                bs = v;
-                bn = n;
-            }
+            const uint64_t k = order_key(pool_r[x], pool_n[x]);
+            if (k < pprev) best = key_max(best, k);
         }
-        wave_best(bs, bn);
-        r_last = bs;
-        n_last = bn;
-        if ((r & (WAVE - 1)) == lane) mine = bn;   // R <= 16 here: one pick per lane
+        best = wave_max_key(best);
+        pprev = best;
+        if (r == lane) mine = key_id(best);
     }
     // ascending: a pick's slot is the number of smaller picks
     int rank = 0;
@@ -199,15 +275,32 @@ __global__ __launch_bounds__(DR_THREADS) void k_decode_route(
     for (int r = nsel + lane; r < R; r += WAVE) out[r] = -1;
 }
 
-constexpr int DA_THREADS = 256;
+constexpr int DA_THREADS = 512;
 constexpr int DA_WAVES = DA_THREADS / WAVE;
 
 size_t decode_attend_lds(const Shape &s) {
     return (size_t)(s.d + DA_WAVES * (WAVE + 2 + s.d)) * 4 + (size_t)(s.R + s.L) * 4;
 }
 
-// One workgroup per (batch, q-head).  Logits in base 2: q is pre-scaled by
-// log2(e)/sqrt(d).
+// DPL consecutive elements starting at i, as floats.
+template <bool BF16, int DPL>
+__device__ __forceinline__ void load_run(const void *base, size_t i, float (&x)[DPL]) {
+    if constexpr (BF16 && DPL == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const u16 *>(base) + i);
+        x[0] = __uint_as_float(w << 16);
+        x[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else if constexpr (!BF16 && DPL == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(reinterpret_cast<const float *>(base) + i);
+        x[0] = v.x;
+        x[1] = v.y;
+    } else {
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) x[j] = load1<BF16>(base, i + j);
+    }
+}
+
+// One workgroup per (batch, q-head), 8 waves.  Logits in base 2: q is
+// pre-scaled by log2(e)/sqrt(d).  Lane l owns output dims DPL l .. DPL l + DPL-1.
 template <int D, bool BF16>
 __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
     Shape s, int pos, const void *__restrict__ q, const void *__restrict__ kc,
@@ -256,72 +349,91 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
     const size_t rs = (size_t)s.Hkv * D;          // cache row stride (elements)
     const size_t base = ((size_t)b * s.T * s.Hkv + g) * D;
     float *p_s = pw + wave * WAVE;
+    // QK: four lanes per key (lane quad kq = lane / 4 takes key 16 j + kq in
+    // sub-pass j), each lane a quarter of the rotation pairs
+    constexpr int PPL = H / 4;                    // rotation pairs per lane
+    const int part = lane & 3, kq = lane >> 2;
     for (int it = wave; it < nitems; it += DA_WAVES) {
         const int bk = blk[it / per_blk];
         if (bk < 0) continue;
         const int s0 = bk * s.beta + (it % per_blk) * WAVE;
         if (s0 > pos) continue;
-        const int key = s0 + lane;
-        const bool valid = key <= pos;
-        float logit = -INFINITY;
-        if (valid) {
-            const size_t ko = base + (size_t)key * rs;
-            const float *cr = cos_t + (size_t)key * H, *sr = sin_t + (size_t)key * H;
-            float acc = 0.0f;
-            for (int i = 0; i < H; i += 4) {
-                float x0[4], x1[4];
-                if constexpr (BF16) {
-                    const uint2 u0 = *reinterpret_cast<const uint2 *>(
-                        reinterpret_cast<const u16 *>(kc) + ko + i);
-                    const uint2 u1 = *reinterpret_cast<const uint2 *>(
-                        reinterpret_cast<const u16 *>(kc) + ko + i + H);
-                    x0[0] = __uint_as_float(u0.x << 16); x0[1] = __uint_as_float(u0.x & 0xFFFF0000u);
-                    x0[2] = __uint_as_float(u0.y << 16); x0[3] = __uint_as_float(u0.y & 0xFFFF0000u);
-                    x1[0] = __uint_as_float(u1.x << 16); x1[1] = __uint_as_float(u1.x & 0xFFFF0000u);
-                    x1[2] = __uint_as_float(u1.y << 16); x1[3] = __uint_as_float(u1.y & 0xFFFF0000u);
-                } else {
-                    const float4 f0 = *reinterpret_cast<const float4 *>(
-                        reinterpret_cast<const float *>(kc) + ko + i);
-                    const float4 f1 = *reinterpret_cast<const float4 *>(
-                        reinterpret_cast<const float *>(kc) + ko + i + H);
-                    x0[0] = f0.x; x0[1] = f0.y; x0[2] = f0.z; x0[3] = f0.w;
-                    x1[0] = f1.x; x1[1] = f1.y; x1[2] = f1.z; x1[3] = f1.w;
-                }
-                const float4 c4 = *reinterpret_cast<const float4 *>(cr + i);
-                const float4 s4 = *reinterpret_cast<const float4 *>(sr + i);
-                const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+        float lg[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float k0 = x0[e] * cc[e] - x1[e] * ss[e];
-                    const float k1 = x1[e] * cc[e] + x0[e] * ss[e];
-                    acc = fmaf(qr[i + e], k0, acc);
-                    acc = fmaf(qr[i + e + H], k1, acc);
+        for (int j = 0; j < 4; ++j) {
+            const int key = s0 + 16 * j + kq;
+            float acc = 0.0f;
+            if (key <= pos) {
+                const size_t ko = base + (size_t)key * rs + part * PPL;
+                const float *cr = cos_t + (size_t)key * H + part * PPL;
+                const float *sr = sin_t + (size_t)key * H + part * PPL;
+#pragma unroll
+                for (int i = 0; i < PPL; i += 4) {
+                    float x0[4], x1[4];
+                    if constexpr (BF16) {
+                        const uint2 u0 = *reinterpret_cast<const uint2 *>(
+                            reinterpret_cast<const u16 *>(kc) + ko + i);
+                        const uint2 u1 = *reinterpret_cast<const uint2 *>(
+                            reinterpret_cast<const u16 *>(kc) + ko + i + H);
+                        x0[0] = __uint_as_float(u0.x << 16); x0[1] = __uint_as_float(u0.x & 0xFFFF0000u);
+                        x0[2] = __uint_as_float(u0.y << 16); x0[3] = __uint_as_float(u0.y & 0xFFFF0000u);
+                        x1[0] = __uint_as_float(u1.x << 16); x1[1] = __uint_as_float(u1.x & 0xFFFF0000u);
+                        x1[2] = __uint_as_float(u1.y << 16); x1[3] = __uint_as_float(u1.y & 0xFFFF0000u);
+                    } else {
+                        const float4 f0 = *reinterpret_cast<const float4 *>(
+                            reinterpret_cast<const float *>(kc) + ko + i);
+                        const float4 f1 = *reinterpret_cast<const float4 *>(
+                            reinterpret_cast<const float *>(kc) + ko + i + H);
+                        x0[0] = f0.x; x0[1] = f0.y; x0[2] = f0.z; x0[3] = f0.w;
+                        x1[0] = f1.x; x1[1] = f1.y; x1[2] = f1.z; x1[3] = f1.w;
+                    }
+                    const float4 c4 = *reinterpret_cast<const float4 *>(cr + i);
+                    const float4 s4 = *reinterpret_cast<const float4 *>(sr + i);
+                    const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+                    const int i0 = part * PPL + i;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float k0 = x0[e] * cc[e] - x1[e] * ss[e];
+                        const float k1 = x1[e] * cc[e] + x0[e] * ss[e];
+                        acc = fmaf(qr[i0 + e], k0, acc);
+                        acc = fmaf(qr[i0 + e + H], k1, acc);
+                    }
                 }
             }
-            logit = acc;
+            // sum over the lane quad
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, false));
+            lg[j] = key <= pos ? acc : -INFINITY;
         }
-        float mx = logit;
+        float mx = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
 #pragma unroll
-        for (int o2 = 32; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+        for (int o2 = 32; o2 > 2; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
         const float mnew = fmaxf(m, mx);          // finite: key s0 <= pos is valid
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // exp2(-inf) = 0
-        const float p = valid ? __builtin_amdgcn_exp2f(logit - mnew) : 0.0f;
-        float ps = p;
+        float ps = 0.0f;
 #pragma unroll
-        for (int o2 = 32; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2);
+        for (int j = 0; j < 4; ++j) {
+            const float p = __builtin_amdgcn_exp2f(lg[j] - mnew);   // 0 past pos
+            ps += p;
+            if (part == 0) p_s[16 * j + kq] = p;
+        }
+#pragma unroll
+        for (int o2 = 32; o2 > 2; o2 >>= 1) ps += __shfl_xor(ps, o2);
         l = l * alpha + ps;
         m = mnew;
 #pragma unroll
         for (int j = 0; j < DPL; ++j) o[j] *= alpha;
-        p_s[lane] = p;
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
-        const int nk = min(WAVE, pos - s0 + 1);
-        for (int kk = 0; kk < nk; ++kk) {
-            const float pk = p_s[kk];
-            const size_t vo = base + (size_t)(s0 + kk) * rs;
+        // rows past pos carry p = 0 and read row pos instead (finite values)
+        const int klast = pos - s0;
 #pragma unroll
-            for (int j = 0; j < DPL; ++j) o[j] = fmaf(pk, load1<BF16>(vc, vo + lane + j * WAVE), o[j]);
+        for (int kk = 0; kk < WAVE; ++kk) {
+            const float pk = p_s[kk];
+            float x[DPL];
+            load_run<BF16, DPL>(vc, base + (size_t)(s0 + min(kk, klast)) * rs + DPL * lane, x);
+#pragma unroll
+            for (int j = 0; j < DPL; ++j) o[j] = fmaf(pk, x[j], o[j]);
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -331,7 +443,7 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
         ml[2 * wave + 1] = l;
     }
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) ow[wave * D + lane + j * WAVE] = o[j];
+    for (int j = 0; j < DPL; ++j) ow[wave * D + DPL * lane + j] = o[j];
     __syncthreads();
     if (wave == 0) {
         float M = -INFINITY;
@@ -345,11 +457,11 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
             const float f = __builtin_amdgcn_exp2f(mw - M);
             lt += f * ml[2 * w + 1];
 #pragma unroll
-            for (int j = 0; j < DPL; ++j) acc[j] += f * ow[w * D + lane + j * WAVE];
+            for (int j = 0; j < DPL; ++j) acc[j] += f * ow[w * D + DPL * lane + j];
         }
         const float inv = 1.0f / lt;
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) store1<BF16>(out, qoff + lane + j * WAVE, acc[j] * inv);
+        for (int j = 0; j < DPL; ++j) store1<BF16>(out, qoff + DPL * lane + j, acc[j] * inv);
     }
 }
 
@@ -367,10 +479,18 @@ hipError_t run_decode(const Shape &s, int pos, const void *q, const void *kc, co
                       hipStream_t st) {
     const unsigned routes = (unsigned)(s.B * s.Hq);
     const size_t lr = decode_route_lds(s);
-    hipError_t e = lds_at_least(k_decode_route<D, BF16>, lr);
-    if (e != hipSuccess) return e;
-    k_decode_route<D, BF16><<<routes, DR_THREADS, lr, st>>>(s, pos, q, cos_t, sin_t, cb, kbar,
-                                                            offsets, entries, sel);
+    hipError_t e;
+    if (s.P == 1) {
+        e = lds_at_least(k_decode_route<D, 1, BF16>, lr);
+        if (e != hipSuccess) return e;
+        k_decode_route<D, 1, BF16><<<routes, DR_THREADS, lr, st>>>(s, pos, q, cos_t, sin_t, cb,
+                                                                   kbar, offsets, entries, sel);
+    } else {
+        e = lds_at_least(k_decode_route<D, 2, BF16>, lr);
+        if (e != hipSuccess) return e;
+        k_decode_route<D, 2, BF16><<<routes, DR_THREADS, lr, st>>>(s, pos, q, cos_t, sin_t, cb,
+                                                                   kbar, offsets, entries, sel);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t la = decode_attend_lds(s);
