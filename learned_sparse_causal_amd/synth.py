@@ -151,3 +151,35 @@ def stress_keys(cfg: Config, kind, seed=7):
         if kind == "two_clusters" and K > 1:
             cb[:, p, 1, :] = -e
     return _cast(k, cfg.dtype), np.ascontiguousarray(cb, np.float32)
+
+
+def concentrated_keys(cfg: Config, seed, model_seed=40, n_topics=8, shared=1.0, topic=0.5,
+                      noise=0.3):
+    """Keys whose block summaries crowd onto few addresses under random
+    codebooks, standing in for the concentrated key distributions of real
+    models (the capacity run of the report page).  Per kv-head, a shared
+    direction and n_topics topic directions live on the slowest-rotating
+    rotary pairs (so they survive the block mean); every block of a sequence
+    takes one topic at random; each token adds N(0, noise^2) in every dim.
+    The shared and topic directions and the codebooks depend on model_seed
+    only, so sequences drawn with different `seed` come from one
+    distribution (a training split and a held-out split).
+    Returns (k [B,T,Hkv,d] in the workload dtype, codebooks [Hkv,P,K,d/P])."""
+    mrng = np.random.Generator(np.random.PCG64(model_seed))
+    srng = np.random.Generator(np.random.PCG64(seed))
+    B, T, Hkv, d = cfg.B, cfg.T, cfg.Hkv, cfg.d
+    h = d // 2
+    slow = np.concatenate([np.arange(h - 4, h), np.arange(d - 4, d)])   # 4 slowest pairs
+    mu = np.zeros((Hkv, d), np.float32)
+    mu[:, h - 1] = shared
+    mu[:, d - 1] = 0.5 * shared
+    nu = np.zeros((Hkv, n_topics, d), np.float32)
+    v = mrng.standard_normal((Hkv, n_topics, len(slow))).astype(np.float32)
+    nu[:, :, slow] = topic * v / np.linalg.norm(v, axis=-1, keepdims=True)
+    cb = codebooks(cfg, mrng)
+    pick = srng.integers(0, n_topics, (B, cfg.NB, Hkv))
+    k = noise * srng.standard_normal((B, T, Hkv, d), dtype=np.float32)
+    for g in range(Hkv):
+        blockwise = mu[g][None, None, :] + nu[g][pick[:, :, g]]          # [B, NB, d]
+        k[:, :, g, :] += np.repeat(blockwise, cfg.beta, axis=1)
+    return _cast(k, cfg.dtype), cb

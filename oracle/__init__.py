@@ -23,5 +23,6 @@ from .binding import (  # noqa: F401
     num_addresses,
     max_threads,
     mixer,
+    calibrate,
 )
 from .dense_twin import dense_masked_attention, dense_causal_attention  # noqa: F401

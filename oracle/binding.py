@@ -55,9 +55,10 @@ def load():
         lib.orc_build_index.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I]
         lib.orc_route.argtypes = [P, P, P, P, P, P, P, P, P, L, P, P, I]
         lib.orc_attention.argtypes = [P, P, P, P, P, P, P, P, L, P, I]
+        lib.orc_calibrate.argtypes = [I, I, I, I, I, I, P, P, I]
         lib.orc_max_threads.restype = I
         for f in ("orc_rope_table", "orc_block_addresses", "orc_posting_lists",
-                  "orc_build_index", "orc_route", "orc_attention"):
+                  "orc_build_index", "orc_route", "orc_attention", "orc_calibrate"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -153,6 +154,17 @@ def route(sh, q, cos, sin, codebooks, index, route_ids=None, nthreads=None):
                      _p(offsets), _p(entries), _p(ids), int(n), _p(sel), _p(gaps),
                      int(nthreads or max_threads()))
     return sel, gaps
+
+
+def calibrate(kbar, codebooks, n_iter):
+    """Spherical k-means calibration of codebooks [Hkv, P, K, d/P] on block
+    summaries kbar [B, Hkv, NB, d]; returns the calibrated codebooks."""
+    kbar = _f32(kbar)
+    B, Hkv, NB, d = kbar.shape
+    cb = np.array(codebooks, np.float32, copy=True, order="C")
+    _, P, K, _ = cb.shape
+    load().orc_calibrate(B, Hkv, NB, d, P, K, _p(kbar), _p(cb), int(n_iter))
+    return cb
 
 
 def attention(sh, q, k, v, cos, sin, sel, route_ids=None, nthreads=None):

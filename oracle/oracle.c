@@ -386,6 +386,70 @@ void orc_route(const orc_shape *sh, const float *q, const float *cos_tab,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Spherical codebook calibration.
+ * [TR] "Capacity" (and Figure 3): calibrating the codebooks spherically on a
+ * training split removes the held-out capacity overflow and lowers the
+ * largest list load.  The pages name the method only.  Reading: spherical
+ * k-means, separately for every kv-head g and component p, over the block
+ * summaries of the training split restricted to component p's sub-vector
+ * (exactly the vectors whose code decisions make the addresses):
+ *   assignment  each point takes the code with the largest inner product
+ *               (fmaf chain in dimension order, ties to the lowest code),
+ *               the decision the address uses;
+ *   update      every code with members becomes the sum of its members
+ *               (fp32 additions in point order from 0.0f) divided by that
+ *               sum's norm, sqrtf of its fmaf-chain square; a code without
+ *               members keeps its value;
+ *   n_iter rounds of assignment followed by update.
+ * kbar: [B][Hkv][NB][d], points ordered batch-major then block; codebooks:
+ * [Hkv][P][K][d/P], calibrated in place. */
+void orc_calibrate(int B, int Hkv, int NB, int d, int P, int K, const float *kbar,
+                   float *codebooks, int n_iter)
+{
+    const int ds = d / P;
+    const long N = (long)B * NB;
+    int32_t *asg = (int32_t *)malloc(sizeof(int32_t) * (size_t)N);
+    float *sum = (float *)malloc(sizeof(float) * (size_t)K * ds);
+    int32_t *cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    for (int g = 0; g < Hkv; ++g) {
+        for (int p = 0; p < P; ++p) {
+            float *C = codebooks + ((size_t)g * P + p) * K * ds;
+            for (int it = 0; it < n_iter; ++it) {
+                for (long i = 0; i < N; ++i) {
+                    long b = i / NB, n = i % NB;
+                    const float *x = kbar + (((size_t)b * Hkv + g) * NB + n) * d + (size_t)p * ds;
+                    int best = 0;
+                    float bs = dot_f32(x, C, ds);
+                    for (int c = 1; c < K; ++c) {
+                        float v = dot_f32(x, C + (size_t)c * ds, ds);
+                        if (v > bs) { bs = v; best = c; }
+                    }
+                    asg[i] = best;
+                }
+                for (size_t e = 0; e < (size_t)K * ds; ++e) sum[e] = 0.0f;
+                for (int c = 0; c < K; ++c) cnt[c] = 0;
+                for (long i = 0; i < N; ++i) {
+                    long b = i / NB, n = i % NB;
+                    const float *x = kbar + (((size_t)b * Hkv + g) * NB + n) * d + (size_t)p * ds;
+                    float *sc = sum + (size_t)asg[i] * ds;
+                    for (int j = 0; j < ds; ++j) sc[j] = sc[j] + x[j];
+                    cnt[asg[i]] += 1;
+                }
+                for (int c = 0; c < K; ++c) {
+                    if (cnt[c] == 0) continue;
+                    const float *sc = sum + (size_t)c * ds;
+                    float norm = sqrtf(dot_f32(sc, sc, ds));
+                    for (int j = 0; j < ds; ++j) C[(size_t)c * ds + j] = sc[j] / norm;
+                }
+            }
+        }
+    }
+    free(asg);
+    free(sum);
+    free(cnt);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Selected-set attention for a list of routes.
  * [TR] "Mixer": local blocks are added separately and attention over the
  * selected set is ordinary causal softmax; no value summary replaces the

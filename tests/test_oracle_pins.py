@@ -474,3 +474,116 @@ def test_bypass_boundary_with_overflowed_blocks(orc):
         E = max(0, qb - cfg.L + 1)
         want = ([0, 1] if E == 2 else [0, -1] if E == 1 else [-1, -1]) if E <= 2 else [0, -1]
         assert sel[:, :, t].tolist() == [[want] * cfg.Hq] * cfg.B, (t, sel[:, :, t])
+
+
+# ------------------------------------------------------ codebook calibration ----
+def unit(x):
+    x = np.asarray(x, np.float64)
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def test_calibrate_single_code_is_normalized_sum(orc):
+    """K = 1: every point joins the one code, so one round leaves the
+    normalized sum of all points (closed form), whatever the start."""
+    rng = np.random.default_rng(31)
+    kbar = rng.standard_normal((2, 3, 5, 8)).astype(np.float32)   # B, Hkv, NB, d
+    cb0 = unit(rng.standard_normal((3, 2, 1, 4))).astype(np.float32)
+    cb = orc.calibrate(kbar, cb0, 1)
+    for g in range(3):
+        for p in range(2):
+            pts = kbar[:, g, :, 4 * p:4 * p + 4].reshape(-1, 4).astype(np.float64)
+            want = unit(pts.sum(0))
+            np.testing.assert_allclose(cb[g, p, 0], want, atol=2e-6)
+
+
+def test_calibrate_zero_rounds_is_identity(orc):
+    rng = np.random.default_rng(32)
+    kbar = rng.standard_normal((1, 2, 6, 8)).astype(np.float32)
+    cb0 = unit(rng.standard_normal((2, 2, 3, 4))).astype(np.float32)
+    assert np.array_equal(orc.calibrate(kbar, cb0, 0), cb0)
+
+
+def clustered_points(rng, dirs, n_per, noise):
+    pts, lab = [], []
+    for c, u in enumerate(dirs):
+        pts.append(u[None, :] + noise * rng.standard_normal((n_per, len(u))))
+        lab += [c] * n_per
+    pts = np.concatenate(pts)
+    perm = rng.permutation(len(pts))
+    return pts[perm].astype(np.float32), np.array(lab)[perm]
+
+
+def test_calibrate_recovers_separated_clusters(orc):
+    """Points around four orthogonal directions, codes started as rotated
+    guesses: calibration assigns every point to its own cluster and ends at a
+    fixed point where each code is the normalized mean of its members
+    (recomputed here in fp64) and each point takes its nearest code."""
+    rng = np.random.default_rng(33)
+    ds, K = 8, 4
+    dirs = np.eye(ds)[:K]
+    pts, lab = clustered_points(rng, dirs, 40, 0.05)          # 160 points
+    kbar = pts.reshape(1, 1, -1, ds)                          # B=1, Hkv=1, NB=160, d=ds, P=1
+    start = unit(dirs + 0.6 * rng.standard_normal((K, ds)))
+    cb = orc.calibrate(kbar, start.reshape(1, 1, K, ds).astype(np.float32), 20)[0, 0]
+    scores = pts.astype(np.float64) @ cb.T.astype(np.float64)
+    asg = scores.argmax(1)
+    # every cluster maps to one code, one to one
+    mapping = {c: set(asg[lab == c]) for c in range(K)}
+    assert all(len(v) == 1 for v in mapping.values())
+    assert len(set.union(*mapping.values())) == K
+    cluster_of = {next(iter(v)): k for k, v in mapping.items()}
+    for c in range(K):
+        members = pts[asg == c].astype(np.float64)
+        np.testing.assert_allclose(cb[c], unit(members.sum(0)), atol=3e-6)
+        assert float(cb[c] @ dirs[cluster_of[c]]) > 0.99
+
+
+def test_calibrate_objective_never_decreases_and_codes_stay_unit(orc):
+    """Spherical k-means: neither the assignment nor the normalized-mean
+    update lowers sum_x max_c <x, c>; every code with members has unit norm;
+    a code that no point is nearest to keeps its value."""
+    rng = np.random.default_rng(34)
+    B, Hkv, NB, d, P, K = 2, 2, 64, 16, 2, 6
+    kbar = (rng.standard_normal((B, Hkv, NB, d)) + 0.8).astype(np.float32)   # skewed cloud
+    cb0 = unit(rng.standard_normal((Hkv, P, K, d // P)))
+    cb0[1, 0, K - 1] = -unit(np.ones(d // P))      # points away from every point
+    cb0 = cb0.astype(np.float32)
+    ds = d // P
+
+    def objective(cb):
+        tot = 0.0
+        for g in range(Hkv):
+            for p in range(P):
+                x = kbar[:, g, :, p * ds:(p + 1) * ds].reshape(-1, ds).astype(np.float64)
+                tot += (x @ cb[g, p].T.astype(np.float64)).max(1).sum()
+        return tot
+
+    prev = objective(cb0)
+    for it in range(1, 9):
+        cb = orc.calibrate(kbar, cb0, it)
+        cur = objective(cb)
+        assert cur >= prev - 1e-4 * abs(prev), (it, prev, cur)
+        prev = cur
+        norms = np.linalg.norm(cb.astype(np.float64), axis=-1)
+        moved = np.abs(cb - cb0).max(-1) > 0
+        assert np.abs(norms[moved] - 1.0).max() < 2e-6
+    assert np.array_equal(cb[1, 0, K - 1], cb0[1, 0, K - 1])
+
+
+def test_calibrate_lowers_overflow_on_concentrated_keys(orc):
+    """The effect the report page shows (section "Capacity", Figure 3), on
+    synthetic concentrated keys: with random codebooks almost every block of
+    a held-out sequence lands on one address and overflows; codebooks
+    calibrated on separate training sequences spread the same blocks."""
+    cfg = configs.SMALL.with_(T=2048, Hq=2, Hkv=2, K=8, cap=8, dtype="f32")
+    train_k, cb0 = synth.concentrated_keys(cfg.with_(B=4), seed=41)
+    test_k, _ = synth.concentrated_keys(cfg, seed=42)
+    c, s = orc.rope_table(cfg.T, cfg.d)
+    sh = orc.Shape.of(**cfg.shape_kw())
+    before = orc.build_index(sh, test_k, c, s, cb0)
+    train_idx = orc.build_index(orc.Shape.of(**cfg.with_(B=4).shape_kw()), train_k, c, s, cb0)
+    cb = orc.calibrate(train_idx["kbar"], cb0, 10)
+    after = orc.build_index(sh, test_k, c, s, cb)
+    assert before["overflow"].sum() > 0
+    assert after["overflow"].sum() < before["overflow"].sum()
+    assert after["load"].max() < before["load"].max()
