@@ -100,7 +100,8 @@ enum {
     MONO_WS_ROUTE = 1,
     MONO_WS_ATTENTION = 2,
     MONO_WS_MIXER = 3,
-    MONO_WS_DENSE = 4
+    MONO_WS_DENSE = 4,
+    MONO_WS_CALIBRATE = 5
 };
 
 /* Bytes of workspace the call `which` needs for `cfg` (0 if it needs none or
@@ -191,6 +192,26 @@ mono_status mono_selected_attention(const mono_config *cfg, const void *q, const
 mono_status mono_dense_attention(const mono_config *cfg, const void *q, const void *k,
                                  const void *v, const float *rope_cos, const float *rope_sin,
                                  void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Spherical codebook calibration (report page, section "Capacity" and
+ * Figure 3: calibrating the codebooks spherically on a training split
+ * removes held-out list overflow and lowers the largest load).
+ *   kbar       [B][Hkv][NB][d] float  block summaries of the training split
+ *              (mono_build_index of the training sequences; B sequences of
+ *              T = cfg->seq_len tokens)
+ *   codebooks  [Hkv][P][K][d/P] float  in: initial codes; out: calibrated
+ *   n_iter     rounds, 0 .. 10000 (0 leaves the codes unchanged)
+ * For every kv-head and component: spherical k-means over the summaries'
+ * component sub-vectors.  Each round assigns every point to the code of
+ * largest inner product (fp32 fused multiply-add chain in dimension order,
+ * lowest code on ties: the address decision) and replaces every code that
+ * has members by the fp32 sum of its members in point order (batch-major,
+ * then block) divided by the correctly rounded square root of that sum's
+ * fused-multiply-add square; a code without members is kept.  Deterministic
+ * and bit-identical to that sequential evaluation.  MONO_ERR_SHAPE if n_iter
+ * is out of range.  Workspace: MONO_WS_CALIBRATE. */
+mono_status mono_calibrate_codebooks(const mono_config *cfg, const float *kbar, float *codebooks,
+                                     int32_t n_iter, void *ws, size_t ws_bytes, void *stream);
 
 /* Incremental index for decoding (news page, section "Learned Routing Faces
  * Dense Attention's Reliability Advantage": a deployed decoder updates its

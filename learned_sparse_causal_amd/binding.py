@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmono.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "mono.h")
 
 MONO_F32, MONO_BF16 = 0, 1
-WS_BUILD, WS_ROUTE, WS_ATTENTION, WS_MIXER, WS_DENSE = 0, 1, 2, 3, 4
+WS_BUILD, WS_ROUTE, WS_ATTENTION, WS_MIXER, WS_DENSE, WS_CALIBRATE = 0, 1, 2, 3, 4, 5
 STATUS = {0: "MONO_OK", 1: "MONO_ERR_NULL", 2: "MONO_ERR_SHAPE", 3: "MONO_ERR_UNSUPPORTED",
           4: "MONO_ERR_WORKSPACE", 5: "MONO_ERR_HIP"}
 
@@ -62,6 +62,7 @@ def load_library(path=LIB_PATH):
     lib.mono_route.argtypes = [cfgp, P, P, P, P, idxp, P, P, S, P]
     lib.mono_selected_attention.argtypes = [cfgp, P, P, P, P, P, P, P, P, S, P]
     lib.mono_dense_attention.argtypes = [cfgp, P, P, P, P, P, P, P, S, P]
+    lib.mono_calibrate_codebooks.argtypes = [cfgp, P, P, ctypes.c_int32, P, S, P]
     lib.mono_decode_index.argtypes = [cfgp, P, P, P, P, idxp, ctypes.c_int32, ctypes.c_int32, P]
     lib.mono_decode_step.argtypes = [cfgp, P, P, P, P, P, P, idxp, ctypes.c_int32, P, P, P]
     lib.mono_mixer_forward.argtypes = [cfgp, P, P, P, P, P, P, P, P, P, S, P]
@@ -69,7 +70,8 @@ def load_library(path=LIB_PATH):
     lib.mono_status_string.argtypes = [I]
     lib.mono_status_string.restype = ctypes.c_char_p
     for f in ("mono_rope_table", "mono_build_index", "mono_route", "mono_selected_attention",
-              "mono_dense_attention", "mono_decode_index", "mono_decode_step",
+              "mono_dense_attention", "mono_calibrate_codebooks", "mono_decode_index",
+              "mono_decode_step",
               "mono_mixer_forward", "mono_mixer_layout"):
         getattr(lib, f).restype = I
     _lib = lib
@@ -241,6 +243,20 @@ def dense_attention(cfg, q, k, v, rope_cos, rope_sin, out=None, ws=None):
                                                ws.data_ptr() if ws is not None else None,
                                                nws, _stream()))
     return out
+
+
+def calibrate_codebooks(cfg, kbar, codebooks, n_iter, ws=None):
+    """mono_calibrate_codebooks: calibrates codebooks [Hkv, P, K, d/P] in place on
+    the training summaries kbar [B, Hkv, NB, d]; returns codebooks."""
+    torch = _torch()
+    c = make_config(cfg)
+    ws, nws = _workspace(cfg, WS_CALIBRATE, ws)
+    args = (_need(kbar, (cfg.B, cfg.Hkv, cfg.NB, cfg.d), torch.float32, "kbar"),
+            _need(codebooks, (cfg.Hkv, cfg.P, cfg.K, cfg.d // cfg.P), torch.float32, "codebooks"))
+    _check(load_library().mono_calibrate_codebooks(ctypes.byref(c), *args, int(n_iter),
+                                                   ws.data_ptr() if ws is not None else None,
+                                                   nws, _stream()))
+    return codebooks
 
 
 def decode_index(cfg, k_cache, rope_cos, rope_sin, codebooks, index, n_indexed, n_tokens):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmono.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["capi.cpp", "build_index.hip", "route.hip", "attention.hip", "decode.hip", "gemm.hip"]
+SOURCES = ["capi.cpp", "build_index.hip", "route.hip", "attention.hip", "decode.hip", "calibrate.hip", "gemm.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -36,6 +36,9 @@ hipError_t launch_decode(const Shape &s, int pos, const void *q, const void *kc,
                          const float *kbar, const int32_t *offsets, const int32_t *entries,
                          int32_t *sel, void *out, hipStream_t st);
 size_t dense_ws_layout(const Shape &s, size_t *off);
+size_t calibrate_ws_bytes(const Shape &s);
+hipError_t launch_calibrate(const Shape &s, int n_iter, const float *kbar, float *codebooks,
+                            void *ws, hipStream_t st);
 hipError_t launch_dense(const Shape &s, const void *q, const void *k, const void *v,
                         const float *cos_t, const float *sin_t, void *out, void *ws,
                         hipStream_t st);
@@ -146,6 +149,8 @@ size_t mono_workspace_bytes(const mono_config *cfg, int which) {
             return mixer_layout(s, off);
         case MONO_WS_DENSE:
             return dense_ws_layout(s, off);
+        case MONO_WS_CALIBRATE:
+            return calibrate_ws_bytes(s);
         default:
             return 0;
     }
@@ -222,6 +227,18 @@ mono_status mono_dense_attention(const mono_config *cfg, const void *q, const vo
     if (ws_bytes < dense_ws_layout(s, off)) return MONO_ERR_WORKSPACE;
     return hip_status(launch_dense(s, q, k, v, rope_cos, rope_sin, out, ws,
                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+mono_status mono_calibrate_codebooks(const mono_config *cfg, const float *kbar, float *codebooks,
+                                     int32_t n_iter, void *ws, size_t ws_bytes, void *stream) {
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!kbar || !codebooks || !ws) return MONO_ERR_NULL;
+    if (n_iter < 0 || n_iter > 10000) return MONO_ERR_SHAPE;
+    if (ws_bytes < calibrate_ws_bytes(s)) return MONO_ERR_WORKSPACE;
+    return hip_status(launch_calibrate(s, n_iter, kbar, codebooks, ws,
+                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
 mono_status mono_decode_index(const mono_config *cfg, const void *k_cache, const float *rope_cos,

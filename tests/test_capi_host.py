@@ -85,6 +85,8 @@ def test_workspace_sizes(lib):
         assert attn >= nent * (cfg.d * es + 12)
         mix = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_MIXER)
         assert mix > attn
+        cal = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_CALIBRATE)
+        assert cal == cfg.Hkv * cfg.P * 2 * cfg.B * cfg.NB * 4
         dense = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_DENSE)
         assert dense >= cfg.B * cfg.T * (cfg.Hq + cfg.Hkv) * cfg.d * es
         off = binding.mixer_layout(cfg)
@@ -113,6 +115,17 @@ def test_attention_and_mixer_argument_errors(lib):
     assert lib.mono_dense_attention(ctypes.byref(c), one, one, one, one, one, one, one, need - 1,
                                     None) == 4
     assert lib.mono_status_string(4) == b"workspace too small"
+
+
+def test_calibrate_argument_errors(lib):
+    cfg = configs.TINY
+    c = binding.make_config(cfg)
+    one = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    need = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_CALIBRATE)
+    assert lib.mono_calibrate_codebooks(ctypes.byref(c), None, one, 3, one, need, None) == 1
+    assert lib.mono_calibrate_codebooks(ctypes.byref(c), one, one, -1, one, need, None) == 2
+    assert lib.mono_calibrate_codebooks(ctypes.byref(c), one, one, 10001, one, need, None) == 2
+    assert lib.mono_calibrate_codebooks(ctypes.byref(c), one, one, 3, one, need - 1, None) == 4
 
 
 def test_decode_argument_errors(lib):
