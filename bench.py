@@ -10,11 +10,13 @@ events recorded around its launches inside the timed steps), the per-stage
 floors, the 4K-32K sweep exponent, the routed step against the dense causal
 attention kernel (mono_dense_attention) at 4K-64K tokens, one decode step
 (mono_decode_step) and index update (mono_decode_index) on the batch-8
-64K-token cache, and the CPU oracle timed on the host cores.
+64K-token cache, spherical codebook calibration (mono_calibrate_codebooks) on
+the 8192-token capacity workload with held-out overflow before and after, and
+the CPU oracle timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-dense]
-                    [--dense-sizes 4096,...] [--no-decode] [--no-cpu-baseline]
-                    [--copy-calibration]
+                    [--dense-sizes 4096,...] [--no-decode] [--no-calibration]
+                    [--no-cpu-baseline] [--copy-calibration]
 
 --copy-calibration runs a plain 256 MiB device copy before the steps; hardware
 counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -203,6 +205,53 @@ def run_decode(cfg, steps=20, warmup=3):
                 * 1e6)
 
 
+def run_calibration(cfg, train_sequences=8, rounds=10, reps=5):
+    """Spherical codebook calibration on the capacity workload: codebooks
+    calibrated on `train_sequences` synthetic concentrated-key sequences
+    (mono_build_index, then mono_calibrate_codebooks timed with HIP events,
+    median of `reps`), and a held-out sequence indexed with the codebooks
+    before and after.  Algorithmic flops per round: 2 K d/P per (point,
+    component) for the assignment plus d/P per point for the sums."""
+    import torch
+    from learned_sparse_causal_amd import binding, synth
+    tcfg = cfg.with_(B=train_sequences)
+    k_train, cb0 = synth.concentrated_keys(tcfg, seed=53)
+    k_test, _ = synth.concentrated_keys(cfg, seed=54)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    cos, sin = binding.device_rope(cfg)
+    cb0_d = torch.from_numpy(cb0).cuda()
+    tidx = binding.build_index(tcfg, torch.from_numpy(k_train).cuda().to(dt), cos, sin, cb0_d)
+    ws = torch.empty(binding.workspace_bytes(tcfg, binding.WS_CALIBRATE), dtype=torch.uint8,
+                     device="cuda")
+    cb = cb0_d.clone()
+    times = []
+    for _ in range(reps + 1):
+        cb.copy_(cb0_d)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        binding.calibrate_codebooks(tcfg, tidx["kbar"], cb, rounds, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    cal_us = float(np.median(times[1:]))
+    kt = torch.from_numpy(k_test).cuda().to(dt)
+    before = binding.build_index(cfg, kt, cos, sin, cb0_d)
+    after = binding.build_index(cfg, kt, cos, sin, cb)
+    torch.cuda.synchronize()
+    n_points = tcfg.B * tcfg.NB
+    flops = rounds * tcfg.Hkv * tcfg.P * n_points * (2 * tcfg.K + 1) * (tcfg.d // tcfg.P)
+    achieved = flops / (cal_us * 1e-6) / 1e12
+    return dict(workload=cfg.name + "_concentrated_keys", train_sequences=train_sequences,
+                rounds=rounds, calibrate_us=cal_us,
+                held_out=dict(overflow_before=int(before["overflow"].sum().item()),
+                              overflow_after=int(after["overflow"].sum().item()),
+                              max_load_before=int(before["load"].max().item()),
+                              max_load_after=int(after["load"].max().item()),
+                              capacity=cfg.cap),
+                roofline=dict(bound="alu", achieved=achieved, peak=FP32_VECTOR_TFLOPS,
+                              unit="TFLOP/s", frac=achieved / FP32_VECTOR_TFLOPS, flops=flops))
+
+
 def dense_flops(cfg):
     """Causal dense attention: 2 d flops for q.k and 2 d for p.v per (query, key <= query)."""
     return 4.0 * cfg.d * cfg.B * cfg.Hq * cfg.T * (cfg.T + 1) / 2
@@ -259,6 +308,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--dense-sizes", default="4096,8192,16384,32768,65536",
                     help="token counts of the routed-vs-dense comparison")
     args = ap.parse_args()
@@ -335,6 +385,8 @@ def main():
         line["dense_vs_routed"] = pts
     if not args.no_decode:
         line["decode"] = run_decode(configs.LARGE)
+    if not args.no_calibration:
+        line["calibration"] = run_calibration(configs.ALL_ELIGIBLE)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

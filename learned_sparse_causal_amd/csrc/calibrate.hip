@@ -16,8 +16,8 @@
 // for a fixed number of rounds.  Every step is the plain sequential fp32
 // operation, so the result is bit-identical to a sequential evaluation.
 //
-// k_calibrate: one workgroup per (kv-head, component).  The codes stay in
-// LDS; each round, threads assign points (the point's sub-vector in
+// k_calibrate: one workgroup per (kv-head, component).  The codes (and,
+// when they fit, the assignments and member lists) stay in LDS; each round, threads assign points (the point's sub-vector in
 // registers), wave 0 lists the members of every code in point order with a
 // ballot counting sort over the code bits, threads sum (code, dim) pairs
 // over those lists, and one thread per code normalizes.
@@ -27,13 +27,22 @@ namespace {
 
 constexpr int CAL_THREADS = 256;
 
+constexpr size_t CAL_LDS_MAX = 150 * 1024;
+
+// Codes, sums (K x ds floats each), counts, starts (K + 1), running ranks;
+// plus the assignments and member lists (N ints each) when they fit.
+size_t calibrate_lds_base(const Shape &s) { return (size_t)(2 * s.K * s.ds + 3 * s.K + 1) * 4; }
+
+bool calibrate_lists_in_lds(const Shape &s) {
+    return calibrate_lds_base(s) + (size_t)2 * s.B * s.NB * 4 <= CAL_LDS_MAX;
+}
+
 size_t calibrate_lds(const Shape &s) {
-    // codes, sums (K x ds floats each), counts, starts (K + 1), running ranks
-    return (size_t)(2 * s.K * s.ds + 3 * s.K + 1) * 4;
+    return calibrate_lds_base(s) + (calibrate_lists_in_lds(s) ? (size_t)2 * s.B * s.NB * 4 : 0);
 }
 
 template <int DS>
-__global__ __launch_bounds__(CAL_THREADS) void k_calibrate(Shape s, int n_iter,
+__global__ __launch_bounds__(CAL_THREADS) void k_calibrate(Shape s, int n_iter, int lists_in_lds,
                                                           const float *__restrict__ kbar,
                                                           float *__restrict__ codebooks,
                                                           int32_t *__restrict__ ws) {
@@ -48,8 +57,8 @@ __global__ __launch_bounds__(CAL_THREADS) void k_calibrate(Shape s, int n_iter,
     const int gp = blockIdx.x;                            // g * P + p
     const int g = gp / P, p = gp % P;
     const int N = s.B * NB;                               // points: batch-major, then block
-    int32_t *asg = ws + (size_t)gp * 2 * N;               // [N] code of each point
-    int32_t *member = asg + N;                            // [N] points grouped by code
+    int32_t *asg = lists_in_lds ? run + K : ws + (size_t)gp * 2 * N;   // [N] code of each point
+    int32_t *member = asg + N;                                        // [N] points grouped by code
     float *cb = codebooks + (size_t)gp * K * DS;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1);
     auto point = [&](int i) {
@@ -124,11 +133,24 @@ __global__ __launch_bounds__(CAL_THREADS) void k_calibrate(Shape s, int n_iter,
             }
         }
         __syncthreads();
-        // sums over the members in point order
+        // sums over the members in point order (eight loads in flight, the
+        // additions still one after another)
         for (int e = tid; e < K * DS; e += CAL_THREADS) {
             const int c = e / DS, j = e % DS;
+            const int m1 = start[c + 1];
             float acc = 0.0f;
-            for (int m = start[c]; m < start[c + 1]; ++m) acc = acc + point(member[m])[j];
+            int m = start[c];
+            for (; m + 8 <= m1; m += 8) {
+                int id[8];
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) id[u] = member[m + u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = point(id[u])[j];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc = acc + v[u];
+            }
+            for (; m < m1; ++m) acc = acc + point(member[m])[j];
             S[e] = acc;
         }
         __syncthreads();
@@ -158,8 +180,8 @@ hipError_t run_calibrate(const Shape &s, int n_iter, const float *kbar, float *c
                                                  (int)lds);
         if (e != hipSuccess) return e;
     }
-    k_calibrate<DS><<<dim3((unsigned)(s.Hkv * s.P)), CAL_THREADS, lds, st>>>(s, n_iter, kbar,
-                                                                           codebooks, ws);
+    k_calibrate<DS><<<dim3((unsigned)(s.Hkv * s.P)), CAL_THREADS, lds, st>>>(
+        s, n_iter, calibrate_lists_in_lds(s) ? 1 : 0, kbar, codebooks, ws);
     return hipGetLastError();
 }
 
