@@ -95,9 +95,16 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     float *sc_s = sc_all + wave * route_wave_floats(PK, DS, MF);
     const int dummy = PK * WAVE * 4;                             // byte offset of a -inf row
 
-    const int h = blockIdx.y, b = blockIdx.z, g = h / s.G;
+    // Work items: (token group, batch, q-head) with the q-heads fastest and
+    // the latest token groups (the longest extension scans) first.  Workgroups
+    // are dealt to the XCDs round-robin, so every XCD gets a mix of heavy and
+    // light groups, and the heads of one token group run at about the same
+    // time and share its rotary-table rows in the caches.
+    const int ngrp = (s.T + nw * WAVE - 1) / (nw * WAVE);
+    const int item = blockIdx.x;
+    const int h = item % s.Hq, b = (item / s.Hq) % s.B, g = h / s.G;
     const size_t ug = (size_t)b * s.Hkv + g;
-    const int tw0 = blockIdx.x * nw * WAVE;                      // first token of the workgroup
+    const int tw0 = (ngrp - 1 - item / (s.Hq * s.B)) * nw * WAVE;   // first token of the workgroup
     const int R = s.R;
     // blocks the workgroup can need: eligible for its last wave
     const int nblk = min(NB, max(0, (min(s.T, tw0 + nw * WAVE) - 1) / s.beta - s.L + 1));
@@ -554,8 +561,7 @@ hipError_t launch_t(const Shape &s, const void *q, const float *cos_t, const flo
                     hipStream_t st) {
     const int waves = route_waves(s, MF);
     const size_t lds = route_lds(s, waves, MF);
-    const dim3 grid((unsigned)((s.T + waves * WAVE - 1) / (waves * WAVE)), (unsigned)s.Hq,
-                    (unsigned)s.B);
+    const dim3 grid((unsigned)((s.T + waves * WAVE - 1) / (waves * WAVE)) * s.Hq * s.B);
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute(
             reinterpret_cast<const void *>(k_route<D, P, NPRM, RM, BF16, MF>),
