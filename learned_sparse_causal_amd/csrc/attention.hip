@@ -358,8 +358,20 @@ __global__ __launch_bounds__(PREP_THREADS) void k_attn_prep(Shape s, const int32
 }
 
 // Rotate every q and k row once into the activation dtype (grid-wide stream;
-// one thread per 4 rotation pairs; rows of one position are adjacent so the
-// rotary table row is read once from cache for all heads).
+// one thread per 8 rotation pairs, so every access is 16 bytes or more; rows
+// of one position are adjacent so the rotary table row is read once from
+// cache for all heads).
+template <bool BF16>
+__device__ __forceinline__ void store8(Elem<BF16> *p, const float *x) {
+    if constexpr (BF16) {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                   pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+    } else {
+        reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+        reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_attn_rotate(Shape s, const void *__restrict__ q,
                                                      const void *__restrict__ k,
@@ -367,12 +379,12 @@ __global__ __launch_bounds__(256) void k_attn_rotate(Shape s, const void *__rest
                                                      const float *__restrict__ sin_t,
                                                      Elem<BF16> *__restrict__ q_rot,
                                                      Elem<BF16> *__restrict__ k_rot) {
-    constexpr int H = D / 2, PT = H / 4;
+    constexpr int H = D / 2, PT = H / 8;
     const int heads = s.Hq + s.Hkv;
     const long total = (long)s.B * s.T * heads * PT;
     for (long task = (long)blockIdx.x * blockDim.x + threadIdx.x; task < total;
          task += (long)gridDim.x * blockDim.x) {
-        const int i = (int)(task % PT) * 4;
+        const int i = (int)(task % PT) * 8;
         const long row = task / PT;               // (b, t, head) with head fastest
         const int hd = (int)(row % heads);
         const long bt = row / heads;
@@ -391,21 +403,23 @@ __global__ __launch_bounds__(256) void k_attn_rotate(Shape s, const void *__rest
         }
         // query rows carry the softmax scale log2(e)/sqrt(d) (base-2 logits)
         const float sc = hd < s.Hq ? 1.4426950408889634f / sqrtf((float)D) : 1.0f;
-        float x0[4], x1[4], o0[4], o1[4];
-        load4<BF16>(src, off + i, x0);
-        load4<BF16>(src, off + i + H, x1);
-        const float4 c = *reinterpret_cast<const float4 *>(cos_t + (size_t)t * H + i);
-        const float4 sn = *reinterpret_cast<const float4 *>(sin_t + (size_t)t * H + i);
-        const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+        float x0[8], x1[8], o0[8], o1[8];
+        load8<BF16>(src, off + i, x0);
+        load8<BF16>(src, off + i + H, x1);
+        const float4 *cp = reinterpret_cast<const float4 *>(cos_t + (size_t)t * H + i);
+        const float4 *sp = reinterpret_cast<const float4 *>(sin_t + (size_t)t * H + i);
+        const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+        const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 8; ++e) {
             const float p0 = x0[e] * cc[e], p1 = x1[e] * ss[e];
             const float p2 = x1[e] * cc[e], p3 = x0[e] * ss[e];
             o0[e] = (p0 - p1) * sc;
             o1[e] = (p2 + p3) * sc;
         }
-        store4(dst + off + i, o0);
-        store4(dst + off + i + H, o1);
+        store8<BF16>(dst + off + i, o0);
+        store8<BF16>(dst + off + i + H, o1);
     }
 }
 
@@ -1309,7 +1323,7 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     const int nwg = (nbins + BIN_WG - 1) / BIN_WG;
     const long ntiles = (long)s.B * s.Hq * (s.T / 64);
     const long nent = (long)s.B * s.Hq * s.T * s.R;
-    const long rot_tasks = (long)s.B * s.T * (s.Hq + s.Hkv) * (D / 8);
+    const long rot_tasks = (long)s.B * s.T * (s.Hq + s.Hkv) * (D / 16);
     k_attn_rotate<D, BF16><<<dim3((unsigned)std::min<long>((rot_tasks + 255) / 256, 65536L)), 256, 0,
                              st>>>(s, q, k, cos_t, sin_t, reinterpret_cast<E *>(w.q_rot),
                                    reinterpret_cast<E *>(w.k_rot));
@@ -1352,7 +1366,7 @@ hipError_t run_dense(const Shape &s, const void *q, const void *k, const void *v
                      const float *cos_t, const float *sin_t, void *out, void *q_rot, void *k_rot,
                      hipStream_t st) {
     using E = Elem<BF16>;
-    const long rot_tasks = (long)s.B * s.T * (s.Hq + s.Hkv) * (D / 8);
+    const long rot_tasks = (long)s.B * s.T * (s.Hq + s.Hkv) * (D / 16);
     k_attn_rotate<D, BF16><<<dim3((unsigned)std::min<long>((rot_tasks + 255) / 256, 65536L)), 256, 0,
                              st>>>(s, q, k, cos_t, sin_t, reinterpret_cast<E *>(q_rot),
                                    reinterpret_cast<E *>(k_rot));
