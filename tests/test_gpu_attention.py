@@ -31,7 +31,9 @@ CFGS = [configs.TINY, configs.SMALL, configs.sweep(4096),
         configs.SMALL.with_(name="d128_beta128", d=128, beta=128, T=4096, Hq=4, Hkv=1, R=8),
         configs.SMALL.with_(name="d128_beta64_f32", d=128, T=2048, Hq=2, Hkv=2, dtype="f32"),
         configs.SMALL.with_(name="d64_beta128_f32", beta=128, T=2048, Hq=2, Hkv=1, dtype="f32",
-                            R=3)]
+                            R=3),
+        # T not a multiple of the 1024-token prep segment or 256-row chunks; batch 2
+        configs.SMALL.with_(name="ragged_T4160_B2", T=4160, B=2, Hq=4, Hkv=2, R=3)]
 
 
 @pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
