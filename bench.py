@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the routed attention hot path on one MI355X.
 
-One step = mono_build_index + mono_route + mono_selected_attention over one
-batch of synthetic q, k, v already resident in HBM (the scaling-sweep
+One step = index build + route + selected-set attention (mono_routed_attention,
+which equals mono_build_index + mono_route + mono_selected_attention bit for
+bit) over one batch of synthetic q, k, v already resident in HBM (the scaling-sweep
 workload at T = 32768: batch 1, 16 heads, d 64, block 64, 1024 addresses,
 capacity 64, 4 probes, R = 2 remote + 2 local blocks, bf16).  Prints one JSON
 line: tokens/s, the dominant kernel's roofline (its duration taken from HIP
@@ -87,10 +88,11 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
-def run_gpu(cfg, steps, warmup):
-    """Times `steps` steps between two synchronizations; HIP events recorded on
-    the launch stream around every stage of every timed step give the
-    per-stage (and, for route, per-kernel) device durations."""
+def run_gpu(cfg, steps, warmup, route_events=True):
+    """Times `steps` steps (mono_routed_attention) between two
+    synchronizations; HIP events the library records on the launch stream
+    between the stages of every timed step give the per-stage (and, for
+    route, per-kernel: the route stage launches k_route only) durations."""
     import torch
     from learned_sparse_causal_amd import binding, synth
     d = synth.qkv_device(cfg)
@@ -102,27 +104,45 @@ def run_gpu(cfg, steps, warmup):
     ws = torch.empty(max(1, binding.workspace_bytes(cfg, binding.WS_ATTENTION)), dtype=torch.uint8,
                      device="cuda")
 
+    # mono_routed_attention: index build, route and attention in one call;
+    # arguments are checked and marshalled once, and the library records the
+    # four stage events on the launch stream
+    launch = binding.routed_attention_launcher(cfg, d["q"], d["k"], d["v"], cos, sin, cb, idx,
+                                               sel, out, ws)
+
     def step(ev=None):
-        if ev: ev[0].record()
-        binding.build_index(cfg, d["k"], cos, sin, cb, idx)
-        if ev: ev[1].record()
-        binding.route(cfg, d["q"], cos, sin, cb, idx, sel)
-        if ev: ev[2].record()
-        binding.selected_attention(cfg, d["q"], d["k"], d["v"], cos, sin, sel, out, ws)
-        if ev: ev[3].record()
+        launch(ev)
 
     for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # timed region: one event pair around it and, if asked, the route stage of
+    # every step bracketed by events (each timed event costs the queue a few
+    # microseconds)
+    evs = [[None, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True), None]
+           if route_events else None for _ in range(steps)]
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    r0.record()
     for e in evs:
         step(e)
+    r1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    step_us = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
-    stage = {k: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
+    region_us = r0.elapsed_time(r1) * 1e3 / steps
+    route_us = (float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+                if route_events else None)
+    # stage breakdown and per-step spread: further steps with all four events
+    n_bd = max(3, min(steps, 10))
+    full = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_bd)]
+    for e in full:
+        step(e)
+    torch.cuda.synchronize()
+    step_us = [e[0].elapsed_time(e[3]) * 1e3 for e in full]
+    stage = {k: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in full])) * 1e3
              for i, k in enumerate(("build", "route", "attend"))}
+    stage["route_in_timed_steps"] = route_us
+    stage["step_gpu_us"] = region_us
     stats = dict(overflow=int(idx["overflow"].sum().item()), max_load=int(idx["load"].max().item()),
                  mean_load=float(cfg.NB / cfg.A))
     return wall_ms, stage, step_us, stats, sel
@@ -332,14 +352,15 @@ def main():
         "attend": max(w["attn_bytes"] / (HBM_PEAK_GBS * 1e9),
                       w["attn_flops"] / (BF16_MFMA_TFLOPS * 1e12)),
     }
-    # the dominant single kernel is the router (mono_route launches k_route only)
-    t_route = stage["route"] * 1e-6
+    # the dominant single kernel is the router (the route stage launches
+    # k_route only), timed by events inside the timed steps
+    t_route = stage["route_in_timed_steps"] * 1e-6
     roof = dict(bound="alu", achieved=w["route_flops"] / t_route / 1e12,
                 peak=FP32_VECTOR_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic("k_route")
     roof["kernel"] = "k_route"
-    roof["kernel_us"] = stage["route"]
+    roof["kernel_us"] = stage["route_in_timed_steps"]
     roof["hbm_GBs"] = w["route_bytes"] / t_route / 1e9
     line = dict(
         metric="routed-attn tokens/s (build+route+attend) at T=32K; % HBM/MFMA roofline",
@@ -360,8 +381,8 @@ def main():
     if not args.no_sweep:
         pts = []
         for T in configs.SWEEP_T:
-            _, _, us, _, _ = run_gpu(configs.sweep(T), 3, 1)
-            pts.append((T, float(np.median(us)) * 1e-3))
+            _, st, _, _, _ = run_gpu(configs.sweep(T), 5, 1, route_events=False)
+            pts.append((T, st["step_gpu_us"] * 1e-3))
         routed_ms.update(pts)
         x = np.log([p[0] for p in pts])
         y = np.log([p[1] for p in pts])
@@ -375,8 +396,8 @@ def main():
         for T in cmp_t:
             c = configs.sweep(T)
             if T not in routed_ms:
-                _, _, us, _, _ = run_gpu(c, 3, 1)
-                routed_ms[T] = float(np.median(us)) * 1e-3
+                _, st, _, _, _ = run_gpu(c, 5, 1, route_events=False)
+                routed_ms[T] = st["step_gpu_us"] * 1e-3
             dms = time_dense(c)
             pts[str(T)] = dict(routed_ms=routed_ms[T], dense_ms=dms,
                                dense_over_routed=dms / routed_ms[T],

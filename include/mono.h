@@ -176,6 +176,27 @@ mono_status mono_selected_attention(const mono_config *cfg, const void *q, const
                                     const int32_t *sel, void *out, void *ws, size_t ws_bytes,
                                     void *stream);
 
+/* The whole routed step in one call: mono_build_index, mono_route and
+ * mono_selected_attention on the same inputs, with identical results.  The
+ * index build and the router also write the rotated key and query rows the
+ * attention needs (they compute them anyway), so the attention's own
+ * rotation pass is skipped.
+ *   q, k, v, rope_cos, rope_sin, codebooks  as for the three calls
+ *   idx      index arrays, filled as by mono_build_index
+ *   sel      [B][Hq][T][R] int32  output, as from mono_route
+ *   out      [B][T][Hq][d] dtype  output, as from mono_selected_attention
+ *   stage_events  NULL, or 4 hipEvent_t slots (created by the caller; a NULL
+ *            slot is skipped) recorded on `stream` before the index build,
+ *            after it, after the route and after the attention (stage timing
+ *            without extra launches; every timed event costs the queue a few
+ *            microseconds)
+ * Workspace: MONO_WS_ATTENTION. */
+mono_status mono_routed_attention(const mono_config *cfg, const void *q, const void *k,
+                                  const void *v, const float *rope_cos, const float *rope_sin,
+                                  const float *codebooks, const mono_index *idx, int32_t *sel,
+                                  void *out, void *ws, size_t ws_bytes, void *const *stage_events,
+                                  void *stream);
+
 /* Dense causal attention, the baseline the routed path is measured against
  * (news page, section "The 99.35 Percent Result Does Not Establish Language
  * Quality": a comparison with optimized FlashAttention-style dense kernels is

@@ -62,6 +62,7 @@ def load_library(path=LIB_PATH):
     lib.mono_route.argtypes = [cfgp, P, P, P, P, idxp, P, P, S, P]
     lib.mono_selected_attention.argtypes = [cfgp, P, P, P, P, P, P, P, P, S, P]
     lib.mono_dense_attention.argtypes = [cfgp, P, P, P, P, P, P, P, S, P]
+    lib.mono_routed_attention.argtypes = [cfgp, P, P, P, P, P, P, idxp, P, P, P, S, P, P]
     lib.mono_calibrate_codebooks.argtypes = [cfgp, P, P, ctypes.c_int32, P, S, P]
     lib.mono_decode_index.argtypes = [cfgp, P, P, P, P, idxp, ctypes.c_int32, ctypes.c_int32, P]
     lib.mono_decode_step.argtypes = [cfgp, P, P, P, P, P, P, idxp, ctypes.c_int32, P, P, P]
@@ -70,7 +71,8 @@ def load_library(path=LIB_PATH):
     lib.mono_status_string.argtypes = [I]
     lib.mono_status_string.restype = ctypes.c_char_p
     for f in ("mono_rope_table", "mono_build_index", "mono_route", "mono_selected_attention",
-              "mono_dense_attention", "mono_calibrate_codebooks", "mono_decode_index",
+              "mono_dense_attention", "mono_routed_attention", "mono_calibrate_codebooks",
+              "mono_decode_index",
               "mono_decode_step",
               "mono_mixer_forward", "mono_mixer_layout"):
         getattr(lib, f).restype = I
@@ -223,6 +225,90 @@ def selected_attention(cfg, q, k, v, rope_cos, rope_sin, sel, out=None, ws=None)
                                                   ws.data_ptr() if ws is not None else None,
                                                   nws, _stream()))
     return out
+
+
+def _event_handles(events):
+    """hipEvent_t handles of four torch.cuda.Event slots (None: not recorded)."""
+    handles = []
+    for e in events:
+        if e is None:
+            handles.append(None)
+            continue
+        if e.cuda_event == 0:       # created on first record
+            e.record()
+        handles.append(e.cuda_event)
+    return handles
+
+
+def routed_attention(cfg, q, k, v, rope_cos, rope_sin, codebooks, index=None, sel=None, out=None,
+                     ws=None, stage_events=None):
+    """mono_routed_attention: the whole step (index build, route, attention) in
+    one call; returns (index, sel, out).  stage_events: None or four slots,
+    each None or a torch.cuda.Event(enable_timing=True), recorded by the
+    library before the build, after it, after the route and after the
+    attention."""
+    torch = _torch()
+    c = make_config(cfg)
+    dt = _act_dtype(cfg)
+    idx = index if index is not None else empty_index(cfg)
+    st = _index_struct(cfg, idx)
+    if sel is None:
+        sel = torch.empty((cfg.B, cfg.Hq, cfg.T, cfg.R), dtype=torch.int32, device="cuda")
+    if out is None:
+        out = torch.empty((cfg.B, cfg.T, cfg.Hq, cfg.d), dtype=dt, device="cuda")
+    ws, nws = _workspace(cfg, WS_ATTENTION, ws)
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * 4)(*_event_handles(stage_events))
+    args = (_need(q, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "q"),
+            _need(k, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "k"),
+            _need(v, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "v"),
+            _need(rope_cos, (cfg.T, cfg.d // 2), torch.float32, "rope_cos"),
+            _need(rope_sin, (cfg.T, cfg.d // 2), torch.float32, "rope_sin"),
+            _need(codebooks, (cfg.Hkv, cfg.P, cfg.K, cfg.d // cfg.P), torch.float32, "codebooks"))
+    _check(load_library().mono_routed_attention(
+        ctypes.byref(c), *args, ctypes.byref(st),
+        _need(sel, (cfg.B, cfg.Hq, cfg.T, cfg.R), torch.int32, "sel"),
+        _need(out, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "out"),
+        ws.data_ptr() if ws is not None else None, nws, ev, _stream()))
+    return idx, sel, out
+
+
+def routed_attention_launcher(cfg, q, k, v, rope_cos, rope_sin, codebooks, index, sel, out, ws):
+    """mono_routed_attention with the arguments checked and marshalled once:
+    returns launch(stage_events=None), which only calls the library (on the
+    stream current when the launcher was made).  For loops that repeat the
+    same call, where per-call checks would cost host time."""
+    torch = _torch()
+    c = make_config(cfg)
+    dt = _act_dtype(cfg)
+    st = _index_struct(cfg, index)
+    ws, nws = _workspace(cfg, WS_ATTENTION, ws)
+    args = (ctypes.byref(c),
+            _need(q, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "q"),
+            _need(k, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "k"),
+            _need(v, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "v"),
+            _need(rope_cos, (cfg.T, cfg.d // 2), torch.float32, "rope_cos"),
+            _need(rope_sin, (cfg.T, cfg.d // 2), torch.float32, "rope_sin"),
+            _need(codebooks, (cfg.Hkv, cfg.P, cfg.K, cfg.d // cfg.P), torch.float32, "codebooks"),
+            ctypes.byref(st),
+            _need(sel, (cfg.B, cfg.Hq, cfg.T, cfg.R), torch.int32, "sel"),
+            _need(out, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "out"),
+            ws.data_ptr() if ws is not None else None, nws)
+    stream = _stream()
+    fn = load_library().mono_routed_attention
+    keep = (c, st, ws)   # referenced by the closure so the marshalled memory stays alive
+
+    def launch(stage_events=None):
+        ev = None
+        if stage_events is not None:
+            ev = (ctypes.c_void_p * 4)(*_event_handles(stage_events))
+        code = fn(*args, ev, stream)
+        if code != 0:
+            _check(code)
+        return keep
+
+    return launch
 
 
 def dense_attention(cfg, q, k, v, rope_cos, rope_sin, out=None, ws=None):

@@ -1277,22 +1277,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 
 template <typename F>
 hipError_t ensure_lds(F *fn, size_t bytes) {
-    if (bytes <= 65536) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    return mono_lds_limit(reinterpret_cast<const void *>(fn), bytes);
 }
 
 // Workgroups for a persistent launch: as many as fit on the device at once
 // (occupancy of `fn` at 256 threads and `lds` bytes), at most `items`.
 template <typename F>
 unsigned persistent_grid(F *fn, size_t lds, long items) {
-    int dev = 0, cus = 256, per_cu = 1;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn),
-                                                     256, lds) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    const long g = (long)cus * per_cu;
+    const long g = mono_resident_workgroups(reinterpret_cast<const void *>(fn), 256, lds);
     return (unsigned)std::max(1L, std::min(items, g));
 }
 
@@ -1315,7 +1307,7 @@ long max_chunks(const Shape &s) {
 template <int D, int BETA, bool BF16>
 hipError_t run_attention(const Shape &s, const void *q, const void *k, const void *v,
                          const float *cos_t, const float *sin_t, const int32_t *sel, void *out,
-                         const AttnWs &w, hipStream_t st) {
+                         const AttnWs &w, hipStream_t st, bool prerotated) {
     using T = Tile<D, BF16>;
     using E = Elem<BF16>;
     const int nbins = s.B * s.Hkv * s.NB;
@@ -1323,10 +1315,13 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     const int nwg = (nbins + BIN_WG - 1) / BIN_WG;
     const long ntiles = (long)s.B * s.Hq * (s.T / 64);
     const long nent = (long)s.B * s.Hq * s.T * s.R;
-    const long rot_tasks = (long)s.B * s.T * (s.Hq + s.Hkv) * (D / 16);
-    k_attn_rotate<D, BF16><<<dim3((unsigned)std::min<long>((rot_tasks + 255) / 256, 65536L)), 256, 0,
-                             st>>>(s, q, k, cos_t, sin_t, reinterpret_cast<E *>(w.q_rot),
-                                   reinterpret_cast<E *>(w.k_rot));
+    if (!prerotated) {
+        const long rot_tasks = (long)s.B * s.T * (s.Hq + s.Hkv) * (D / 16);
+        k_attn_rotate<D, BF16><<<dim3((unsigned)std::min<long>((rot_tasks + 255) / 256, 65536L)),
+                                 256, 0, st>>>(s, q, k, cos_t, sin_t,
+                                               reinterpret_cast<E *>(w.q_rot),
+                                               reinterpret_cast<E *>(w.k_rot));
+    }
     hipError_t err = ensure_lds(k_attn_prep, (size_t)s.NB * sizeof(int));
     if (err != hipSuccess) return err;
     k_attn_prep<<<dim3((unsigned)nseg, (unsigned)s.Hkv, (unsigned)s.B), PREP_THREADS,
@@ -1434,9 +1429,20 @@ size_t attention_ws_layout(const Shape &s, size_t *off) {
     return p;
 }
 
+// prerotated: the workspace's rotated-q and rotated-k slots (attention_rot_slots)
+// already hold the rows, so the rotation pass is skipped.
+// Rotated-q and rotated-k slots of the attention workspace.
+void attention_rot_slots(const Shape &s, void *ws, void **q_rot, void **k_rot) {
+    size_t off[14];
+    attention_ws_layout(s, off);
+    unsigned char *base = reinterpret_cast<unsigned char *>(ws);
+    *q_rot = base + off[11];
+    *k_rot = base + off[12];
+}
+
 hipError_t launch_attention(const Shape &s, const void *q, const void *k, const void *v,
                             const float *cos_t, const float *sin_t, const int32_t *sel, void *out,
-                            void *ws, hipStream_t st) {
+                            void *ws, hipStream_t st, bool prerotated) {
     size_t off[14];
     attention_ws_layout(s, off);
     unsigned char *base = reinterpret_cast<unsigned char *>(ws);
@@ -1456,7 +1462,7 @@ hipError_t launch_attention(const Shape &s, const void *q, const void *k, const 
     w.list_q = reinterpret_cast<int32_t *>(base + off[13]);
     w.wg_first = reinterpret_cast<int32_t *>(base + off[8]);
     const bool bf = s.dtype == 1;
-#define MONO_ATTN_ARGS s, q, k, v, cos_t, sin_t, sel, out, w, st
+#define MONO_ATTN_ARGS s, q, k, v, cos_t, sin_t, sel, out, w, st, prerotated
     if (s.d == 64) {
         if (s.beta == 64) return bf ? run_attention<64, 64, true>(MONO_ATTN_ARGS)
                                     : run_attention<64, 64, false>(MONO_ATTN_ARGS);

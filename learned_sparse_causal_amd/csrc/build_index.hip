@@ -61,7 +61,8 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
                                                               const float *__restrict__ sin_t,
                                                               const float *__restrict__ cb,
                                                               float *__restrict__ kbar,
-                                                              int32_t *__restrict__ addr) {
+                                                              int32_t *__restrict__ addr,
+                                                              void *__restrict__ k_rot) {
     constexpr int H = D / 2;
     constexpr int DS = D / P;
     constexpr int ES = BF16 ? 2 : 4;
@@ -135,12 +136,28 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
                     }
                     const float cc = cs[u * H + i], ss = sn[u * H + i];
                     const float p0 = x0 * cc, p1 = x1 * ss, p2 = x1 * cc, p3 = x0 * ss;
-                    a0[j] = a0[j] + (p0 - p1);
-                    a1[j] = a1[j] + (p2 + p3);
+                    const float r0 = p0 - p1, r1 = p2 + p3;
+                    a0[j] = a0[j] + r0;
+                    a1[j] = a1[j] + r1;
+                    if (k_rot) {   // the rotated pair replaces the staged one (this thread's)
+                        if constexpr (BF16) {
+                            reinterpret_cast<u16 *>(rows)[e] = f32_to_bf16_bits(r0);
+                            reinterpret_cast<u16 *>(rows)[e + H] = f32_to_bf16_bits(r1);
+                        } else {
+                            reinterpret_cast<float *>(rows)[e] = r0;
+                            reinterpret_cast<float *>(rows)[e + H] = r1;
+                        }
+                    }
                 }
             }
         }
         __syncthreads();
+        if (k_rot) {   // the chunk's rotated rows, rounded to the activation dtype
+            u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(k_rot) +
+                                                   ((size_t)b * s.T + t0 + c) * rowE * ES);
+            for (int v = tid; v < vecs; v += BA_THREADS) dst[v] = reinterpret_cast<const u32x4 *>(rows)[v];
+            __syncthreads();   // read before the next chunk overwrites the rows
+        }
     }
 #undef MONO_BA_FETCH
 
@@ -309,27 +326,24 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
 template <int D, int P, bool BF16, int MAXP>
 hipError_t launch_ba_t(const Shape &s, int n0, int n1, int ct, size_t lds, const void *k,
                        const float *cos_t, const float *sin_t, const float *cb, float *kbar,
-                       int32_t *addr, hipStream_t st) {
+                       int32_t *addr, void *k_rot, hipStream_t st) {
     auto *fn = k_block_address<D, P, BF16, MAXP>;
-    if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    const hipError_t e = mono_lds_limit(reinterpret_cast<const void *>(fn), lds);
+    if (e != hipSuccess) return e;
     fn<<<dim3((unsigned)(n1 - n0), (unsigned)s.B), BA_THREADS, lds, st>>>(s, ct, n0, k, cos_t,
-                                                                          sin_t, cb, kbar, addr);
+                                                                          sin_t, cb, kbar, addr,
+                                                                          k_rot);
     return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_ba(const Shape &s, int n0, int n1, const void *k, const float *cos_t,
                      const float *sin_t, const float *cb, float *kbar, int32_t *addr,
-                     hipStream_t st) {
+                     void *k_rot, hipStream_t st) {
     const int ct = block_chunk_tokens(s);
     const size_t lds = block_address_lds(s, ct);
     const bool small = s.Hkv * (D / 2) <= 2 * BA_THREADS;
-#define MONO_BA_ARGS s, n0, n1, ct, lds, k, cos_t, sin_t, cb, kbar, addr, st
+#define MONO_BA_ARGS s, n0, n1, ct, lds, k, cos_t, sin_t, cb, kbar, addr, k_rot, st
     if (s.P == 1)
         return small ? launch_ba_t<D, 1, BF16, 2>(MONO_BA_ARGS)
                      : launch_ba_t<D, 1, BF16, 8>(MONO_BA_ARGS);
@@ -340,23 +354,26 @@ hipError_t launch_ba(const Shape &s, int n0, int n1, const void *k, const float 
 
 }  // namespace
 
-// Summaries and addresses of blocks n0 .. n1-1 of every sequence.
+// Summaries and addresses of blocks n0 .. n1-1 of every sequence; with k_rot
+// non-null also the rotated keys of those blocks ([B][T][Hkv][d], activation
+// dtype).
 hipError_t launch_block_address_range(const Shape &s, int n0, int n1, const void *k,
                                       const float *cos_t, const float *sin_t, const float *cb,
-                                      float *kbar, int32_t *addr, hipStream_t st) {
+                                      float *kbar, int32_t *addr, hipStream_t st,
+                                      void *k_rot = nullptr) {
     if (n1 <= n0) return hipSuccess;
     const bool bf = s.dtype == 1;
     if (s.d == 64)
-        return bf ? launch_ba<64, true>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, st)
-                  : launch_ba<64, false>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, st);
-    return bf ? launch_ba<128, true>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, st)
-              : launch_ba<128, false>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, st);
+        return bf ? launch_ba<64, true>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, k_rot, st)
+                  : launch_ba<64, false>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, k_rot, st);
+    return bf ? launch_ba<128, true>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, k_rot, st)
+              : launch_ba<128, false>(s, n0, n1, k, cos_t, sin_t, cb, kbar, addr, k_rot, st);
 }
 
 hipError_t launch_block_address(const Shape &s, const void *k, const float *cos_t,
                                 const float *sin_t, const float *cb, float *kbar, int32_t *addr,
-                                hipStream_t st) {
-    return launch_block_address_range(s, 0, s.NB, k, cos_t, sin_t, cb, kbar, addr, st);
+                                hipStream_t st, void *k_rot) {
+    return launch_block_address_range(s, 0, s.NB, k, cos_t, sin_t, cb, kbar, addr, st, k_rot);
 }
 
 // Lists of blocks 0 .. nbu-1 (the indexed prefix of every sequence).

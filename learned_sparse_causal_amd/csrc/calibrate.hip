@@ -174,12 +174,8 @@ template <int DS>
 hipError_t run_calibrate(const Shape &s, int n_iter, const float *kbar, float *codebooks,
                          int32_t *ws, hipStream_t st) {
     const size_t lds = calibrate_lds(s);
-    if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_calibrate<DS>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    const hipError_t e = mono_lds_limit(reinterpret_cast<const void *>(k_calibrate<DS>), lds);
+    if (e != hipSuccess) return e;
     k_calibrate<DS><<<dim3((unsigned)(s.Hkv * s.P)), CAL_THREADS, lds, st>>>(
         s, n_iter, calibrate_lists_in_lds(s) ? 1 : 0, kbar, codebooks, ws);
     return hipGetLastError();

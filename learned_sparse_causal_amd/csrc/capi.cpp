@@ -6,13 +6,16 @@
 
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "common.hpp"
 #include "mono.h"
 
 hipError_t launch_block_address(const Shape &s, const void *k, const float *cos_t,
                                 const float *sin_t, const float *cb, float *kbar, int32_t *addr,
-                                hipStream_t st);
+                                hipStream_t st, void *k_rot = nullptr);
 hipError_t launch_posting_lists(const Shape &s, const int32_t *addr, int32_t *offsets,
                                 int32_t *entries, int32_t *load, int32_t *overflow, hipStream_t st);
 hipError_t launch_index_stats(const Shape &s, const int32_t *overflow, const int32_t *load,
@@ -20,14 +23,16 @@ hipError_t launch_index_stats(const Shape &s, const int32_t *overflow, const int
 hipError_t launch_route(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
                         const float *cb, const float *kbar, const int32_t *addr,
                         const int32_t *offsets, const int32_t *entries, const int32_t *load,
-                        int32_t *sel, hipStream_t st);
+                        int32_t *sel, hipStream_t st, void *q_rot = nullptr);
 size_t attention_ws_layout(const Shape &s, size_t *off);
 hipError_t launch_attention(const Shape &s, const void *q, const void *k, const void *v,
                             const float *cos_t, const float *sin_t, const int32_t *sel, void *out,
-                            void *ws, hipStream_t st);
+                            void *ws, hipStream_t st, bool prerotated = false);
+void attention_rot_slots(const Shape &s, void *ws, void **q_rot, void **k_rot);
 hipError_t launch_block_address_range(const Shape &s, int n0, int n1, const void *k,
                                       const float *cos_t, const float *sin_t, const float *cb,
-                                      float *kbar, int32_t *addr, hipStream_t st);
+                                      float *kbar, int32_t *addr, hipStream_t st,
+                                      void *k_rot = nullptr);
 hipError_t launch_posting_lists_prefix(const Shape &s, int nbu, const int32_t *addr,
                                        int32_t *offsets, int32_t *entries, int32_t *load,
                                        int32_t *overflow, hipStream_t st);
@@ -46,6 +51,42 @@ hipError_t launch_gemm(int bf16, int M, int N, int Kd, const void *A, const void
                        hipStream_t st);
 hipError_t launch_gemm_qkv(int bf16, int M, int N, int Kd, const void *A, const void *Bm, void *q,
                            void *k, void *v, int nq, int nk, hipStream_t st);
+
+namespace {
+std::mutex g_cache_mutex;
+std::map<std::pair<const void *, int>, size_t> g_lds_set;                  // (kernel, device)
+std::map<std::tuple<const void *, int, int, size_t>, long> g_resident;    // (.., threads, lds)
+}  // namespace
+
+hipError_t mono_lds_limit(const void *fn, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    size_t &have = g_lds_set[{fn, dev}];
+    if (have >= bytes) return hipSuccess;
+    const hipError_t e =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) have = bytes;
+    return e;
+}
+
+long mono_resident_workgroups(const void *fn, int threads, size_t lds) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lock(g_cache_mutex);
+    const auto key = std::make_tuple(fn, dev, threads, lds);
+    const auto it = g_resident.find(key);
+    if (it != g_resident.end()) return it->second;
+    int cus = 256, per_cu = 1;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    const long g = (long)cus * per_cu;
+    g_resident[key] = g;
+    return g;
+}
 
 namespace {
 
@@ -216,6 +257,47 @@ mono_status mono_selected_attention(const mono_config *cfg, const void *q, const
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
+mono_status mono_routed_attention(const mono_config *cfg, const void *q, const void *k,
+                                  const void *v, const float *rope_cos, const float *rope_sin,
+                                  const float *codebooks, const mono_index *idx, int32_t *sel,
+                                  void *out, void *ws, size_t ws_bytes, void *const *stage_events,
+                                  void *stream) {
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!q || !k || !v || !rope_cos || !rope_sin || !codebooks || !index_ok(idx) || !sel || !out ||
+        !ws)
+        return MONO_ERR_NULL;
+    size_t off[14];
+    if (ws_bytes < attention_ws_layout(s, off)) return MONO_ERR_WORKSPACE;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+        return stage_events && stage_events[i]
+                   ? hipEventRecord(reinterpret_cast<hipEvent_t>(stage_events[i]), hs)
+                   : hipSuccess;
+    };
+    // every query bypassing the search: the router writes no rotated rows,
+    // the attention rotates them itself
+    const bool fused = s.NB - s.L > s.R;
+    void *q_rot = nullptr, *k_rot = nullptr;
+    if (fused) attention_rot_slots(s, ws, &q_rot, &k_rot);
+    if (mark(0) != hipSuccess) return MONO_ERR_HIP;
+    if (launch_block_address(s, k, rope_cos, rope_sin, codebooks, idx->kbar, idx->addr, hs,
+                             k_rot) != hipSuccess ||
+        launch_posting_lists(s, idx->addr, idx->offsets, idx->entries, idx->load, idx->overflow,
+                             hs) != hipSuccess ||
+        mark(1) != hipSuccess)
+        return MONO_ERR_HIP;
+    if (launch_route(s, q, rope_cos, rope_sin, codebooks, idx->kbar, idx->addr, idx->offsets,
+                     idx->entries, idx->load, sel, hs, q_rot) != hipSuccess ||
+        mark(2) != hipSuccess)
+        return MONO_ERR_HIP;
+    if (launch_attention(s, q, k, v, rope_cos, rope_sin, sel, out, ws, hs, fused) != hipSuccess ||
+        mark(3) != hipSuccess)
+        return MONO_ERR_HIP;
+    return MONO_OK;
+}
+
 mono_status mono_dense_attention(const mono_config *cfg, const void *q, const void *k,
                                  const void *v, const float *rope_cos, const float *rope_sin,
                                  void *out, void *ws, size_t ws_bytes, void *stream) {
@@ -313,7 +395,12 @@ mono_status mono_mixer_forward(const mono_config *cfg, const void *x, const void
     const int nq = s.Hq * s.d, nk = s.Hkv * s.d;
     if (launch_gemm_qkv(bf, M, nq + 2 * nk, s.W, x, w_qkv, q, k, v, nq, nk, hs) != hipSuccess)
         return MONO_ERR_HIP;
-    if (launch_block_address(s, k, rope_cos, rope_sin, codebooks, idx.kbar, idx.addr, hs) !=
+    // the index build and the router also write the attention's rotated rows
+    // (unless every query bypasses the search)
+    const bool fused = s.NB - s.L > s.R;
+    void *q_rot = nullptr, *k_rot = nullptr;
+    if (fused) attention_rot_slots(s, inner, &q_rot, &k_rot);
+    if (launch_block_address(s, k, rope_cos, rope_sin, codebooks, idx.kbar, idx.addr, hs, k_rot) !=
         hipSuccess)
         return MONO_ERR_HIP;
     if (launch_posting_lists(s, idx.addr, idx.offsets, idx.entries, idx.load, idx.overflow, hs) !=
@@ -322,9 +409,10 @@ mono_status mono_mixer_forward(const mono_config *cfg, const void *x, const void
     if (stats && launch_index_stats(s, idx.overflow, idx.load, stats, hs) != hipSuccess)
         return MONO_ERR_HIP;
     if (launch_route(s, q, rope_cos, rope_sin, codebooks, idx.kbar, idx.addr, idx.offsets,
-                     idx.entries, idx.load, sel, hs) != hipSuccess)
+                     idx.entries, idx.load, sel, hs, q_rot) != hipSuccess)
         return MONO_ERR_HIP;
-    if (launch_attention(s, q, k, v, rope_cos, rope_sin, sel, attn, inner, hs) != hipSuccess)
+    if (launch_attention(s, q, k, v, rope_cos, rope_sin, sel, attn, inner, hs, fused) !=
+        hipSuccess)
         return MONO_ERR_HIP;
     return hip_status(launch_gemm(bf, M, s.W, nq, attn, w_o, delta, hs));
 }

@@ -18,6 +18,14 @@ struct Shape {
 
 static constexpr int WAVE = 64;
 
+// Host helpers (defined in capi.cpp), cached per (kernel, device) so that
+// repeated launches make no runtime queries:
+//  - raise a kernel's dynamic LDS limit to at least `bytes` (bytes > 64 KiB);
+//  - workgroups of `threads` threads and `lds` bytes resident at once on the
+//    current device (compute units x occupancy, at least 1).
+hipError_t mono_lds_limit(const void *fn, size_t bytes);
+long mono_resident_workgroups(const void *fn, int threads, size_t lds);
+
 __device__ __forceinline__ float bf16_bits_to_f32(u16 b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }

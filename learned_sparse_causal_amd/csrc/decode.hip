@@ -467,9 +467,7 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
 
 template <typename F>
 hipError_t lds_at_least(F *fn, size_t bytes) {
-    if (bytes <= 65536) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    return mono_lds_limit(reinterpret_cast<const void *>(fn), bytes);
 }
 
 template <int D, bool BF16>

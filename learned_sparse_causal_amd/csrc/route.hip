@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                                                const int32_t *__restrict__ addr,
                                                const int32_t *__restrict__ offsets,
                                                const int32_t *__restrict__ entries,
-                                               int32_t *__restrict__ sel) {
+                                               int32_t *__restrict__ sel,
+                                               void *__restrict__ q_rot) {
     constexpr int H = D / 2;
     constexpr int DS = D / P;
     extern __shared__ float lds[];
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     const int E = max(0, qb - s.L + 1);
     int32_t *out = sel + (((size_t)b * s.Hq + h) * s.T + (live ? t : t0)) * R;
 
-    if (E <= R) {  // bypass: every eligible block is selected
+    if (E <= R && !q_rot) {  // bypass: every eligible block is selected
         if (live)
             for (int r = 0; r < R; ++r) out[r] = r < E ? r : -1;
         return;
@@ -169,6 +170,31 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                 qr[i + e + H] = p2 + p3;
             }
         }
+        // the attention's copy of the row: pre-scaled by log2(e)/sqrt(d) and
+        // rounded to the activation dtype
+        if (q_rot && live) {
+            const float sc = 1.4426950408889634f / sqrtf((float)D);
+            if constexpr (BF16) {
+                u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<u16 *>(q_rot) + base);
+#pragma unroll
+                for (int j = 0; j < D; j += 8)
+                    dst[j / 8] = u32x4{pack_bf16x2(qr[j] * sc, qr[j + 1] * sc),
+                                       pack_bf16x2(qr[j + 2] * sc, qr[j + 3] * sc),
+                                       pack_bf16x2(qr[j + 4] * sc, qr[j + 5] * sc),
+                                       pack_bf16x2(qr[j + 6] * sc, qr[j + 7] * sc)};
+            } else {
+                float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(q_rot) + base);
+#pragma unroll
+                for (int j = 0; j < D; j += 4)
+                    dst[j / 4] = make_float4(qr[j] * sc, qr[j + 1] * sc, qr[j + 2] * sc,
+                                             qr[j + 3] * sc);
+            }
+        }
+    }
+    if (E <= R) {  // bypass: every eligible block is selected
+        if (live)
+            for (int r = 0; r < R; ++r) out[r] = r < E ? r : -1;
+        return;
     }
 
     // ---- component scores; the n_probes best codes of each component
@@ -558,18 +584,15 @@ template <int D, int P, int NPRM, int RM, bool BF16, bool MF>
 hipError_t launch_t(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
                     const float *cb, const float *kbar, const int32_t *addr,
                     const int32_t *offsets, const int32_t *entries, int32_t *sel,
-                    hipStream_t st) {
+                    void *q_rot, hipStream_t st) {
     const int waves = route_waves(s, MF);
     const size_t lds = route_lds(s, waves, MF);
     const dim3 grid((unsigned)((s.T + waves * WAVE - 1) / (waves * WAVE)) * s.Hq * s.B);
-    if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(k_route<D, P, NPRM, RM, BF16, MF>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
+    const hipError_t e =
+        mono_lds_limit(reinterpret_cast<const void *>(k_route<D, P, NPRM, RM, BF16, MF>), lds);
+    if (e != hipSuccess) return e;
     k_route<D, P, NPRM, RM, BF16, MF><<<grid, waves * WAVE, lds, st>>>(
-        s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, sel);
+        s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, sel, q_rot);
     return hipGetLastError();
 }
 
@@ -577,49 +600,49 @@ hipError_t launch_t(const Shape &s, const void *q, const float *cos_t, const flo
 template <int D, int P, int NPRM, int RM, bool BF16>
 hipError_t launch_m(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
                     const float *cb, const float *kbar, const int32_t *addr,
-                    const int32_t *offsets, const int32_t *entries, int32_t *sel,
+                    const int32_t *offsets, const int32_t *entries, int32_t *sel, void *q_rot,
                     hipStream_t st) {
     if constexpr (D == 64 && P == 2) {
         if (s.K <= 32 && route_lds(s, 1, true) <= 160 * 1024)
             return launch_t<D, P, NPRM, RM, BF16, true>(s, q, cos_t, sin_t, cb, kbar, addr,
-                                                        offsets, entries, sel, st);
+                                                        offsets, entries, sel, q_rot, st);
     }
     return launch_t<D, P, NPRM, RM, BF16, false>(s, q, cos_t, sin_t, cb, kbar, addr, offsets,
-                                                 entries, sel, st);
+                                                 entries, sel, q_rot, st);
 }
 
 template <int D, int P, bool BF16>
 hipError_t launch_sel(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
                       const float *cb, const float *kbar, const int32_t *addr,
-                      const int32_t *offsets, const int32_t *entries, int32_t *sel,
+                      const int32_t *offsets, const int32_t *entries, int32_t *sel, void *q_rot,
                       hipStream_t st) {
-    if (s.npr <= 2 && s.R <= 2)
-        return launch_m<D, P, 2, 2, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
-                                          sel, st);
-    if (s.npr <= 4 && s.R <= 2)
-        return launch_m<D, P, 4, 2, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
-                                          sel, st);
-    if (s.npr <= 8 && s.R <= 8)
-        return launch_m<D, P, 8, 8, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
-                                          sel, st);
-    return launch_m<D, P, 16, 16, BF16>(s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries,
-                                        sel, st);
+#define MONO_SEL_ARGS s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, sel, q_rot, st
+    if (s.npr <= 2 && s.R <= 2) return launch_m<D, P, 2, 2, BF16>(MONO_SEL_ARGS);
+    if (s.npr <= 4 && s.R <= 2) return launch_m<D, P, 4, 2, BF16>(MONO_SEL_ARGS);
+    if (s.npr <= 8 && s.R <= 8) return launch_m<D, P, 8, 8, BF16>(MONO_SEL_ARGS);
+    return launch_m<D, P, 16, 16, BF16>(MONO_SEL_ARGS);
+#undef MONO_SEL_ARGS
 }
 
 }  // namespace
 
+// With q_rot non-null the router also writes every query's rotated row for
+// the attention (pre-scaled, activation dtype); a configuration in which
+// every query bypasses the search then returns hipErrorInvalidValue (the
+// caller rotates separately).
 hipError_t launch_route(const Shape &s, const void *q, const float *cos_t, const float *sin_t,
                         const float *cb, const float *kbar, const int32_t *addr,
                         const int32_t *offsets, const int32_t *entries, const int32_t *load,
-                        int32_t *sel, hipStream_t st) {
+                        int32_t *sel, hipStream_t st, void *q_rot) {
     (void)load;
     if (s.NB - s.L <= s.R) {  // every query bypasses the search
+        if (q_rot) return hipErrorInvalidValue;
         const long routes = (long)s.B * s.Hq * s.T;
         k_route_bypass<<<dim3((unsigned)((routes + 255) / 256)), 256, 0, st>>>(s, sel);
         return hipGetLastError();
     }
     const bool bf = s.dtype == 1;
-#define MONO_ROUTE_ARGS s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, sel, st
+#define MONO_ROUTE_ARGS s, q, cos_t, sin_t, cb, kbar, addr, offsets, entries, sel, q_rot, st
     if (s.d == 64) {
         if (s.P == 1) return bf ? launch_sel<64, 1, true>(MONO_ROUTE_ARGS)
                                 : launch_sel<64, 1, false>(MONO_ROUTE_ARGS);
