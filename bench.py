@@ -381,7 +381,7 @@ def main():
     if not args.no_sweep:
         pts = []
         for T in configs.SWEEP_T:
-            _, st, _, _, _ = run_gpu(configs.sweep(T), 5, 1, route_events=False)
+            _, st, _, _, _ = run_gpu(configs.sweep(T), 3, 1, route_events=False)
             pts.append((T, st["step_gpu_us"] * 1e-3))
         routed_ms.update(pts)
         x = np.log([p[0] for p in pts])
@@ -396,7 +396,7 @@ def main():
         for T in cmp_t:
             c = configs.sweep(T)
             if T not in routed_ms:
-                _, st, _, _, _ = run_gpu(c, 5, 1, route_events=False)
+                _, st, _, _, _ = run_gpu(c, 3, 1, route_events=False)
                 routed_ms[T] = st["step_gpu_us"] * 1e-3
             dms = time_dense(c)
             pts[str(T)] = dict(routed_ms=routed_ms[T], dense_ms=dms,
