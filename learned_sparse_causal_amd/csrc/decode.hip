@@ -107,18 +107,19 @@ __device__ __forceinline__ float chain_lds_global(const float *a, const float *_
     return acc;
 }
 
-// Stage n ints from global to LDS, eight loads in flight per lane.
+// Stage n ints from global to LDS, up to SI loads in flight per lane.
+constexpr int SI = 24;
 __device__ __forceinline__ void stage_ints(int *dst, const int32_t *__restrict__ src, int n,
                                            int lane) {
-    for (int b0 = 0; b0 < n; b0 += 8 * WAVE) {
-        int v[8];
+    for (int b0 = 0; b0 < n; b0 += SI * WAVE) {
+        int v[SI];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < SI; ++k) {
             const int i = b0 + k * WAVE + lane;
             v[k] = i < n ? src[i] : 0;
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < SI; ++k) {
             const int i = b0 + k * WAVE + lane;
             if (i < n) dst[i] = v[k];
         }
@@ -155,24 +156,64 @@ __global__ __launch_bounds__(DR_THREADS) void k_decode_route(
         return;
     }
     const size_t u = (size_t)b * s.Hkv + g;
-    // the (batch, kv-head) lists, staged once
+    // Every load that does not depend on another goes out first: this lane's
+    // query pair(s) and rotary values, its codebook row(s) (codes lane and
+    // lane + 64), then the (batch, kv-head) lists staged into LDS.
+    const size_t qoff = (size_t)route * D;
+    constexpr int QP = (H + WAVE - 1) / WAVE;            // query pairs per lane
+    float qa[QP], qb2[QP], qc[QP], qs[QP];
+#pragma unroll
+    for (int k = 0; k < QP; ++k) {
+        const int i = lane + k * WAVE;
+        const bool ok = i < H;
+        qa[k] = ok ? load1<BF16>(q, qoff + i) : 0.0f;
+        qb2[k] = ok ? load1<BF16>(q, qoff + i + H) : 0.0f;
+        qc[k] = ok ? cos_t[(size_t)pos * H + i] : 0.0f;
+        qs[k] = ok ? sin_t[(size_t)pos * H + i] : 0.0f;
+    }
+    float4 crow[2][DS / 4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int x = lane + k * WAVE;
+        const int xc = x < P * K ? x : 0;                 // in bounds; unused past P K
+        const float4 *cr = reinterpret_cast<const float4 *>(
+            cb + (((size_t)g * P + xc / K) * K + xc % K) * DS);
+        if (k == 0 || (P == 2 && P * K > WAVE)) {
+#pragma unroll
+            for (int j = 0; j < DS / 4; ++j) crow[k][j] = cr[j];
+        }
+    }
     stage_ints(off, offsets + u * (A + 1), A + 1, lane);
     stage_ints(ent, entries + u * NB, NB, lane);
     // rotate (fp32, products rounded before the add)
-    const size_t qoff = (size_t)route * D;
-    for (int i = lane; i < H; i += WAVE) {
-        const float a = load1<BF16>(q, qoff + i), bb = load1<BF16>(q, qoff + i + H);
-        const float c = cos_t[(size_t)pos * H + i], sn = sin_t[(size_t)pos * H + i];
-        const float ac = a * c, bs = bb * sn, bc = bb * c, as = a * sn;
-        qr[i] = ac - bs;
-        qr[i + H] = bc + as;
+#pragma unroll
+    for (int k = 0; k < QP; ++k) {
+        const int i = lane + k * WAVE;
+        if (i < H) {
+            const float ac = qa[k] * qc[k], bs = qb2[k] * qs[k];
+            const float bc = qb2[k] * qc[k], as = qa[k] * qs[k];
+            qr[i] = ac - bs;
+            qr[i + H] = bc + as;
+        }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     // code scores: fma chains in dimension order
-    for (int x = lane; x < P * K; x += WAVE) {
-        const int p = x / K;
-        sc[x] = chain_lds_global<DS>(qr + p * DS, cb + (((size_t)g * P + p) * K + x % K) * DS);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int x = lane + k * WAVE;
+        if ((k == 0 || (P == 2 && P * K > WAVE)) && x < P * K) {
+            const float *qp = qr + (x / K) * DS;
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < DS / 4; ++j) {
+                acc = fmaf(qp[4 * j], crow[k][j].x, acc);
+                acc = fmaf(qp[4 * j + 1], crow[k][j].y, acc);
+                acc = fmaf(qp[4 * j + 2], crow[k][j].z, acc);
+                acc = fmaf(qp[4 * j + 3], crow[k][j].w, acc);
+            }
+            sc[x] = acc;
+        }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
@@ -358,6 +399,24 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
         if (bk < 0) continue;
         const int s0 = bk * s.beta + (it % per_blk) * WAVE;
         if (s0 > pos) continue;
+        // the item's value rows (this lane's dims), issued with the keys so
+        // that one wait covers both; rows past pos read row pos (p = 0 there)
+        const int klast = pos - s0;
+        constexpr int RW = BF16 ? 1 : DPL;        // 32-bit words of raw values per key
+        uint32_t vr[WAVE][RW];
+#pragma unroll
+        for (int kk = 0; kk < WAVE; ++kk) {
+            const size_t vo = base + (size_t)(s0 + min(kk, klast)) * rs + DPL * lane;
+            if constexpr (BF16 && DPL == 2) {
+                vr[kk][0] = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const u16 *>(vc) + vo);
+            } else if constexpr (BF16) {
+                vr[kk][0] = reinterpret_cast<const u16 *>(vc)[vo];
+            } else {
+#pragma unroll
+                for (int j = 0; j < DPL; ++j)
+                    vr[kk][j] = __float_as_uint(reinterpret_cast<const float *>(vc)[vo + j]);
+            }
+        }
         float lg[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -425,13 +484,19 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
         for (int j = 0; j < DPL; ++j) o[j] *= alpha;
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
-        // rows past pos carry p = 0 and read row pos instead (finite values)
-        const int klast = pos - s0;
 #pragma unroll
         for (int kk = 0; kk < WAVE; ++kk) {
             const float pk = p_s[kk];
             float x[DPL];
-            load_run<BF16, DPL>(vc, base + (size_t)(s0 + min(kk, klast)) * rs + DPL * lane, x);
+            if constexpr (BF16 && DPL == 2) {
+                x[0] = __uint_as_float(vr[kk][0] << 16);
+                x[1] = __uint_as_float(vr[kk][0] & 0xFFFF0000u);
+            } else if constexpr (BF16) {
+                x[0] = __uint_as_float(vr[kk][0] << 16);
+            } else {
+#pragma unroll
+                for (int j = 0; j < DPL; ++j) x[j] = __uint_as_float(vr[kk][j]);
+            }
 #pragma unroll
             for (int j = 0; j < DPL; ++j) o[j] = fmaf(pk, x[j], o[j]);
         }
