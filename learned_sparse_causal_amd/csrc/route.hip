@@ -63,14 +63,30 @@ __device__ __forceinline__ void insert(u64 (&lst)[M], u64 k) {
     }
 }
 
-// Float offset of the per-wave score areas (after the lists, 16-byte aligned).
-__host__ __device__ constexpr int route_sc_off(int NB, int A) { return (3 * NB + A + 1 + 3) & ~3; }
+// Blocks the extension scan reads past the last eligible one (its row
+// offsets are loaded two batches ahead).
+constexpr int SCAN_U = 8, SCAN_PAD = 2 * SCAN_U;
 
-// Floats of one wave's score area: P*K score rows and a -inf row of 64
-// lanes; with matrix-core scoring it also holds the query transpose.
-__host__ __device__ constexpr int route_wave_floats(int PK, int DS, bool mf) {
-    return mf && 64 * (DS + 4) > (PK + 1) * 64 ? 64 * (DS + 4) : (PK + 1) * 64;
+// Float offset of the per-wave score areas (after the lists, 16-byte aligned).
+__host__ __device__ constexpr int route_sc_off(int NB, int A) {
+    return (3 * NB + 2 * SCAN_PAD + A + 1 + 3) & ~3;
 }
+
+// Floats per score row: 64 lanes plus 4 of padding, so the 16 rows one
+// matrix-core result store writes start on different banks.
+constexpr int SROW = 64 + 4;
+
+// Floats of one wave's score area: P*K score rows and a -inf row; with
+// matrix-core scoring it first holds the wave's 64 rotated rows (SROW
+// floats each, or DS + 4 for the one-component-at-a-time transpose).
+__host__ __device__ constexpr int route_wave_floats(int PK, int DS, bool mf) {
+    return mf && 64 * SROW > (PK + 1) * SROW ? 64 * SROW : (PK + 1) * SROW;
+}
+
+// List offsets and (entry, address) pairs each thread loads per staging
+// round before storing any (a round covers STAGE_OFF * threads offsets and
+// half as many blocks).
+constexpr int STAGE_OFF = 8, STAGE_BLK = STAGE_OFF / 2;
 
 template <int D, int P, int NPRM, int RM, bool BF16, bool MF>
 __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__ q,
@@ -88,13 +104,13 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     extern __shared__ float lds[];
     const int K = s.K, PK = P * K, A = s.A, NB = s.NB;
     const int nw = blockDim.x / WAVE;
-    int2 *meta_s = reinterpret_cast<int2 *>(lds);                // [NB]: score-row offsets
-    int *off_s = reinterpret_cast<int *>(meta_s + NB);           // [A+1]
+    int2 *meta_s = reinterpret_cast<int2 *>(lds);                // [NB + SCAN_PAD]: score-row offsets
+    int *off_s = reinterpret_cast<int *>(meta_s + NB + SCAN_PAD);   // [A+1]
     int *ent_s = off_s + A + 1;                                  // [NB]
     float *sc_all = reinterpret_cast<float *>(lds) + route_sc_off(NB, A);   // [nw][...][64]
-    const int lane = lane_id(), wave = threadIdx.x / WAVE;
+    const int lane = lane_id(), wave = uniform(threadIdx.x / WAVE);
     float *sc_s = sc_all + wave * route_wave_floats(PK, DS, MF);
-    const int dummy = PK * WAVE * 4;                             // byte offset of a -inf row
+    const int dummy = PK * SROW * 4;                             // byte offset of a -inf row
 
     // Work items: (token group, batch, q-head) with the q-heads fastest and
     // the latest token groups (the longest extension scans) first.  Workgroups
@@ -110,35 +126,145 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     // blocks the workgroup can need: eligible for its last wave
     const int nblk = min(NB, max(0, (min(s.T, tw0 + nw * WAVE) - 1) / s.beta - s.L + 1));
     const bool any_search = nblk > R;
+
+    const int t0 = tw0 + wave * WAVE;
+    const int t = t0 + lane;
+    const bool live = t < s.T;
+    const int qb = t0 / s.beta;
+    const int E = max(0, qb - s.L + 1);
+    const int tq = min(t, s.T - 1);        // clamped: the loads below stay in bounds
+    const size_t qbase = (((size_t)b * s.T + tq) * s.Hq + h) * D;
+
+    // List offsets, list entries and block addresses of the (batch,
+    // kv-head) are staged in LDS.  Every thread issues its loads of a round
+    // (indexes clamped, so none is predicated) before storing any; the
+    // addresses go to the row-offset table and are converted below.  The
+    // first round's loads are issued before the wave's own loads, so its
+    // stores wait for them only.
+    const int32_t *off_g = offsets + ug * (A + 1);
+    const int32_t *ent_g = entries + ug * NB;
+    const int32_t *ad_g = addr + ug * NB;
+    int *meta_i = reinterpret_cast<int *>(meta_s);
+    const int bd = blockDim.x, tid = threadIdx.x;
+    int vo[STAGE_OFF], ve[STAGE_BLK], va[STAGE_BLK];
+    auto stage_load = [&](int r0) {
+#pragma unroll
+        for (int u = 0; u < STAGE_OFF; ++u) vo[u] = off_g[min(r0 + u * bd + tid, A)];
+#pragma unroll
+        for (int u = 0; u < STAGE_BLK; ++u) {
+            const int i = min(r0 / 2 + u * bd + tid, NB - 1);
+            ve[u] = ent_g[i];
+            va[u] = ad_g[i];
+        }
+    };
+    // (stores use the same clamped indexes: threads past the end rewrite the
+    // last element with its own value; addresses past nblk are never read)
+    auto stage_store = [&](int r0) {
+#pragma unroll
+        for (int u = 0; u < STAGE_OFF; ++u) off_s[min(r0 + u * bd + tid, A)] = vo[u];
+#pragma unroll
+        for (int u = 0; u < STAGE_BLK; ++u) {
+            const int i = min(r0 / 2 + u * bd + tid, NB - 1);
+            ent_s[i] = ve[u];
+            meta_i[2 * i] = va[u];
+        }
+    };
+    if (any_search) stage_load(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // For d = 64 in bf16 the wave's own global loads come next (the raw
+    // query row, the rotary rows and, for matrix-core scoring, every
+    // codebook operand), so that they are in flight while the workgroup
+    // stages its lists; the barriers below wait for LDS only.  They are
+    // issued by every wave (a predicated load would make the wait counts
+    // after it conservative), and wider rows would hold too many registers
+    // across the staging.
+    constexpr int NTM = MF ? 2 : 1, NSM = MF ? DS / 4 : 1;   // matrix-core: K <= 32
+    // Matrix-core scoring in bf16 loads and rotates the wave's 64 rows
+    // cooperatively: lane l takes rows l/8 + 8j (j < 8) and the rotation
+    // pairs 4(l%8) .. 4(l%8)+3 of each, so one load instruction covers 8
+    // rows instead of 64 (a row per lane touches a cache line per lane).
+    constexpr bool COOP = MF && BF16;
+    constexpr int CJ = COOP ? 8 : 1;
+    constexpr bool EARLY_ROT = D <= 64 && BF16 && !COOP;
+    constexpr int QW = BF16 ? D / 8 : D / 4;                 // 16-byte words of the row
+    constexpr int RW = EARLY_ROT ? H / 4 : 1;
+    u32x4 qraw[QW];
+    float4 cs4[RW], sn4[RW];
+    float bpre[P][NTM][NSM];
+    const float4 *cr = reinterpret_cast<const float4 *>(cos_t + (size_t)tq * H);
+    const float4 *sr = reinterpret_cast<const float4 *>(sin_t + (size_t)tq * H);
+    const u32x4 *qsrc = BF16 ? reinterpret_cast<const u32x4 *>(
+                                   reinterpret_cast<const u16 *>(q) + qbase)
+                             : reinterpret_cast<const u32x4 *>(
+                                   reinterpret_cast<const float *>(q) + qbase);
+    uint2 qlo[CJ], qhi[CJ];
+    float4 cj[CJ], sj[CJ];
+    {
+        if constexpr (COOP) {
+            const int k4 = 4 * (lane & 7);
+#pragma unroll
+            for (int j = 0; j < CJ; ++j) {
+                const int tr = min(t0 + (lane >> 3) + 8 * j, s.T - 1);
+                const u16 *qrow = reinterpret_cast<const u16 *>(q) + (((size_t)b * s.T + tr) * s.Hq + h) * D;
+                qlo[j] = *reinterpret_cast<const uint2 *>(qrow + k4);
+                qhi[j] = *reinterpret_cast<const uint2 *>(qrow + H + k4);
+                cj[j] = *reinterpret_cast<const float4 *>(cos_t + (size_t)tr * H + k4);
+                sj[j] = *reinterpret_cast<const float4 *>(sin_t + (size_t)tr * H + k4);
+            }
+        }
+        if constexpr (EARLY_ROT) {
+#pragma unroll
+            for (int j = 0; j < QW; ++j) qraw[j] = qsrc[j];
+#pragma unroll
+            for (int i = 0; i < RW; ++i) {
+                cs4[i] = cr[i];
+                sn4[i] = sr[i];
+            }
+        }
+        if constexpr (MF) {
+            // B operand of code nt*16 + (lane & 15), dimension 4 st + lane / 16
+            const float *cbg = cb + (size_t)g * PK * DS;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int nt = 0; nt < NTM; ++nt) {
+                    const int code = nt * 16 + (lane & 15);
+                    const float *brow = cbg + (p * K + (code < K ? code : 0)) * DS + (lane >> 4);
+#pragma unroll
+                    for (int st = 0; st < NSM; ++st) bpre[p][nt][st] = brow[4 * st];   // clamped row
+                }
+        }
+    }
+
+    __builtin_amdgcn_sched_barrier(0);
     if (any_search) {
-        const int32_t *off_g = offsets + ug * (A + 1);
-        for (int x = threadIdx.x; x <= A; x += blockDim.x) off_s[x] = off_g[x];
-        const int32_t *ent_g = entries + ug * NB;
-        for (int x = threadIdx.x; x < NB; x += blockDim.x) ent_s[x] = ent_g[x];
+        stage_store(0);
+        for (int r0 = STAGE_OFF * bd; r0 <= A || r0 / 2 < NB; r0 += STAGE_OFF * bd) {
+            stage_load(r0);
+            stage_store(r0);
+        }
     }
     __syncthreads();
     if (any_search) {
-        const int32_t *ad_g = addr + ug * NB;
         for (int n = threadIdx.x; n < nblk; n += blockDim.x) {
-            const int a = ad_g[n];
+            const int a = meta_s[n].x;
             // kept blocks are the first `cap` of the address in source order,
             // so n is indexed iff it is not after the list's last entry.
             // Byte offsets of the score-table rows of the block's component
             // codes; a block that is not indexed points at the -inf row.
             const int c0 = P == 1 ? a : a / K, c1 = P == 1 ? 0 : a - c0 * K;
             const bool idx = n <= ent_s[off_s[a + 1] - 1];
-            const int o0 = c0 * WAVE * 4, o1 = P == 1 ? dummy : (K + c1) * WAVE * 4;
+            const int o0 = c0 * SROW * 4, o1 = P == 1 ? dummy : (K + c1) * SROW * 4;
             meta_s[n] = idx ? make_int2(o0, o1) : make_int2(dummy, dummy);
         }
+        // the scan's read-ahead past the eligible blocks lands on the -inf row
+        for (int n = nblk + (int)threadIdx.x; n < nblk + SCAN_PAD; n += blockDim.x)
+            meta_s[n] = make_int2(dummy, dummy);
     }
     __syncthreads();
 
-    const int t0 = tw0 + wave * WAVE;
     if (t0 >= s.T) return;
-    const int t = t0 + lane;
-    const bool live = t < s.T;
-    const int qb = t0 / s.beta;
-    const int E = max(0, qb - s.L + 1);
     int32_t *out = sel + (((size_t)b * s.Hq + h) * s.T + (live ? t : t0)) * R;
 
     if (E <= R && !q_rot) {  // bypass: every eligible block is selected
@@ -149,17 +275,75 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
 
     // ---- rotated query (fp32, same rounding as the rotation's definition)
     float qr[D];
-    {
-        const size_t base = (((size_t)b * s.T + (live ? t : t0)) * s.Hq + h) * D;
-        float x[D];
+    if constexpr (COOP) {
+        // rotated rows go to the wave's score area, [row][SROW], with
+        // dimension p*DS + 4 st + lg at float p*DS + lg*(DS/4) + st: the
+        // layout the matrix-core A fragments read as float4s
+        constexpr int NS = DS / 4;
+        const int k = lane & 7;
+        const float sc = 1.4426950408889634f / sqrtf((float)D);
 #pragma unroll
-        for (int j = 0; j < D; j += 8) load8<BF16>(q, base + j, x + j);
-        const float *cr = cos_t + (size_t)(live ? t : t0) * H;
-        const float *sr = sin_t + (size_t)(live ? t : t0) * H;
+        for (int j = 0; j < CJ; ++j) {
+            const int r = (lane >> 3) + 8 * j;
+            const uint32_t w[4] = {qlo[j].x, qlo[j].y, qhi[j].x, qhi[j].y};
+            const float lo[4] = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+            const float hi[4] = {__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
+                                 __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u)};
+            const float cc[4] = {cj[j].x, cj[j].y, cj[j].z, cj[j].w};
+            const float ss[4] = {sj[j].x, sj[j].y, sj[j].z, sj[j].w};
+            float rl[4], rh[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = lo[e] * cc[e], p1 = hi[e] * ss[e], p2 = hi[e] * cc[e], p3 = lo[e] * ss[e];
+                rl[e] = p0 - p1;
+                rh[e] = p2 + p3;
+                sc_s[r * SROW + e * NS + k] = rl[e];           // dimension 4k + e
+                sc_s[r * SROW + DS + e * NS + k] = rh[e];      // dimension H + 4k + e
+            }
+            // the attention's copy: pre-scaled by log2(e)/sqrt(d), bf16
+            if (q_rot && t0 + r < s.T) {
+                u16 *dst = reinterpret_cast<u16 *>(q_rot) + (((size_t)b * s.T + t0 + r) * s.Hq + h) * D;
+                *reinterpret_cast<uint2 *>(dst + 4 * k) =
+                    make_uint2(pack_bf16x2(rl[0] * sc, rl[1] * sc), pack_bf16x2(rl[2] * sc, rl[3] * sc));
+                *reinterpret_cast<uint2 *>(dst + H + 4 * k) =
+                    make_uint2(pack_bf16x2(rh[0] * sc, rh[1] * sc), pack_bf16x2(rh[2] * sc, rh[3] * sc));
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // the lane's own row, back in dimension order
+#pragma unroll
+        for (int m = 0; m < D / 4; ++m) {
+            const float4 v = *reinterpret_cast<const float4 *>(sc_s + lane * SROW + 4 * m);
+            const int p = m / 8, lg = (m % 8) / 2, st0 = 4 * (m % 2);
+            qr[p * DS + 4 * (st0 + 0) + lg] = v.x;
+            qr[p * DS + 4 * (st0 + 1) + lg] = v.y;
+            qr[p * DS + 4 * (st0 + 2) + lg] = v.z;
+            qr[p * DS + 4 * (st0 + 3) + lg] = v.w;
+        }
+    } else {
+        float x[D];
+        if constexpr (!EARLY_ROT) {
+#pragma unroll
+            for (int j = 0; j < QW; ++j) qraw[j] = qsrc[j];
+        }
+#pragma unroll
+        for (int j = 0; j < QW; ++j) {
+            const uint32_t w[4] = {qraw[j][0], qraw[j][1], qraw[j][2], qraw[j][3]};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (BF16) {
+                    x[8 * j + 2 * e] = __uint_as_float(w[e] << 16);
+                    x[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                } else {
+                    x[4 * j + e] = __uint_as_float(w[e]);
+                }
+            }
+        }
 #pragma unroll
         for (int i = 0; i < H; i += 4) {
-            const float4 c4 = *reinterpret_cast<const float4 *>(cr + i);
-            const float4 s4 = *reinterpret_cast<const float4 *>(sr + i);
+            const float4 c4 = EARLY_ROT ? cs4[EARLY_ROT ? i / 4 : 0] : cr[i / 4];
+            const float4 s4 = EARLY_ROT ? sn4[EARLY_ROT ? i / 4 : 0] : sr[i / 4];
             const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
             const float ss[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
@@ -175,7 +359,7 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
         if (q_rot && live) {
             const float sc = 1.4426950408889634f / sqrtf((float)D);
             if constexpr (BF16) {
-                u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<u16 *>(q_rot) + base);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<u16 *>(q_rot) + qbase);
 #pragma unroll
                 for (int j = 0; j < D; j += 8)
                     dst[j / 8] = u32x4{pack_bf16x2(qr[j] * sc, qr[j + 1] * sc),
@@ -183,7 +367,7 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                                        pack_bf16x2(qr[j + 4] * sc, qr[j + 5] * sc),
                                        pack_bf16x2(qr[j + 6] * sc, qr[j + 7] * sc)};
             } else {
-                float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(q_rot) + base);
+                float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(q_rot) + qbase);
 #pragma unroll
                 for (int j = 0; j < D; j += 4)
                     dst[j / 4] = make_float4(qr[j] * sc, qr[j + 1] * sc, qr[j + 2] * sc,
@@ -198,10 +382,24 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     }
 
     // ---- component scores; the n_probes best codes of each component
-    // (codes arrive in ascending order, so a strict compare keeps the lower
-    // code first on equal scores)
     float tv[P][NPRM];
     int tc[P][NPRM];
+    // insert (v, c) into a list sorted best first; codes arrive ascending,
+    // so a strict compare keeps the lower code first on equal scores.  Slot
+    // x takes the median of (old slot x-1, old slot x, v).
+    auto top_insert = [](float (&tvp)[NPRM], int (&tcp)[NPRM], float v, int c) {
+        bool bt[NPRM];
+#pragma unroll
+        for (int x = 0; x < NPRM; ++x) bt[x] = v > tvp[x];
+#pragma unroll
+        for (int x = NPRM - 1; x > 0; --x) {
+            const int cx = bt[x] ? c : tcp[x];
+            tcp[x] = bt[x - 1] ? tcp[x - 1] : cx;
+            tvp[x] = __builtin_amdgcn_fmed3f(tvp[x - 1], tvp[x], v);
+        }
+        tcp[0] = bt[0] ? c : tcp[0];
+        tvp[0] = bt[0] ? v : tvp[0];
+    };
     if constexpr (MF) {
         // Matrix cores: per component, D[route][code] = sum_k A[route][k]
         // B[k][code] as a chain of fp32 16x16x4 MFMAs over steps st, with
@@ -215,6 +413,22 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
         constexpr int MT = WAVE / 16, NS = DS / 4;
         constexpr int QTS = DS + 4;                      // transpose row stride (floats)
         float af[P][MT][NS];
+        if constexpr (COOP) {
+            // the rotated rows are already in the A-fragment layout
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int st = 0; st < NS; st += 4) {
+                        const float4 v4 = *reinterpret_cast<const float4 *>(
+                            sc_s + (mt * 16 + lr) * SROW + p * DS + lg * NS + st);
+                        af[p][mt][st] = v4.x;
+                        af[p][mt][st + 1] = v4.y;
+                        af[p][mt][st + 2] = v4.z;
+                        af[p][mt][st + 3] = v4.w;
+                    }
+        } else {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
 #pragma unroll
@@ -236,18 +450,19 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                     af[p][mt][st + 3] = v4.w;
                 }
         }
+        }
         const int NT = (K + 15) / 16;
-        const float *cbg = cb + (size_t)g * PK * DS;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            for (int nt = 0; nt < NT; ++nt) {
-                // B operand: code nt*16 + lr, dimension 4 st + lg (codebook
-                // rows are small and stay in the caches)
+#pragma unroll
+            for (int nt = 0; nt < NTM; ++nt) {
+                if (nt >= NT) break;
+                // B operand (loaded at the start): code nt*16 + lr, dimension
+                // 4 st + lg; columns past the last code are zero
                 const int code = nt * 16 + lr;
-                const float *brow = cbg + (p * K + (code < K ? code : 0)) * DS + lg;
                 float bf[NS];
 #pragma unroll
-                for (int st = 0; st < NS; ++st) bf[st] = code < K ? brow[4 * st] : 0.0f;
+                for (int st = 0; st < NS; ++st) bf[st] = code < K ? bpre[p][nt][st] : 0.0f;
                 f32x4 acc[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -261,7 +476,7 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                 if (code < K) {
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        *reinterpret_cast<float4 *>(sc_s + (p * K + code) * WAVE + mt * 16 + 4 * lg) =
+                        *reinterpret_cast<float4 *>(sc_s + (p * K + code) * SROW + mt * 16 + 4 * lg) =
                             make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
                 }
             }
@@ -271,20 +486,7 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
 #pragma unroll
             for (int x = 0; x < NPRM; ++x) { tv[p][x] = -INFINITY; tc[p][x] = -1; }
 #pragma unroll 4
-            for (int c = 0; c < K; ++c) {
-                float v = sc_s[(p * K + c) * WAVE + lane];
-                int cc = c;
-#pragma unroll
-                for (int x = 0; x < NPRM; ++x) {
-                    const bool sw = v > tv[p][x];
-                    const float ov = tv[p][x];
-                    const int oc = tc[p][x];
-                    tv[p][x] = sw ? v : ov;
-                    tc[p][x] = sw ? cc : oc;
-                    v = sw ? ov : v;
-                    cc = sw ? oc : cc;
-                }
-            }
+            for (int c = 0; c < K; ++c) top_insert(tv[p], tc[p], sc_s[(p * K + c) * SROW + lane], c);
         }
     } else {
     const float *cbg = cb + (size_t)g * PK * DS;
@@ -298,19 +500,8 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
             float acc = 0.0f;
 #pragma unroll
             for (int j = 0; j < DS; ++j) acc = __builtin_fmaf(qr[p * DS + j], crow[j], acc);
-            sc_s[(p * K + c) * WAVE + lane] = acc;
-            float v = acc;
-            int cc = c;
-#pragma unroll
-            for (int x = 0; x < NPRM; ++x) {
-                const bool sw = v > tv[p][x];
-                const float ov = tv[p][x];
-                const int oc = tc[p][x];
-                tv[p][x] = sw ? v : ov;
-                tc[p][x] = sw ? cc : oc;
-                v = sw ? ov : v;
-                cc = sw ? oc : cc;
-            }
+            sc_s[(p * K + c) * SROW + lane] = acc;
+            top_insert(tv[p], tc[p], acc, c);
         }
     }
     }
@@ -405,7 +596,7 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     int cnt = 0;
     if (live) walk_part1([&](int n) { add(n); ++cnt; });
 
-    sc_s[PK * WAVE + lane] = -INFINITY;   // the row unindexed blocks point at
+    sc_s[PK * SROW + lane] = -INFINITY;   // the row unindexed blocks point at
 
     // ---- pool part 2: extension to R blocks, for lanes that need it.  The
     // R best eligible indexed blocks by (sigma desc, block asc), visited in
@@ -433,7 +624,16 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
         // a branch (lanes that need no extension update a list they never
         // read).
         auto visit = [&](float sg, int n) {
-            if (RM <= 2 || (need & (sg > bs[RM - 1]))) {   // short lists: no branch
+            if constexpr (RM == 2) {
+                // two slots: slot 1 takes the median of (slot 0, slot 1,
+                // new); equal values keep the resident
+                const bool b0 = sg > bs[0], b1 = sg > bs[1];
+                const int n1 = b1 ? n : bn[1];
+                bn[1] = b0 ? bn[0] : n1;
+                bn[0] = b0 ? n : bn[0];
+                bs[1] = __builtin_amdgcn_fmed3f(bs[0], bs[1], sg);
+                bs[0] = b0 ? sg : bs[0];
+            } else if (RM <= 2 || (need & (sg > bs[RM - 1]))) {   // short lists: no branch
                 bool beat[RM];
 #pragma unroll
                 for (int x = 0; x < RM; ++x) beat[x] = sg > bs[x];
@@ -446,25 +646,56 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                 bn[0] = beat[0] ? n : bn[0];
             }
         };
-        constexpr int U = 8;
+        // Software pipeline over batches of U blocks: the row offsets are
+        // loaded two batches ahead and the score gathers one batch ahead,
+        // so the visits of a batch overlap the next batch's LDS reads.  The
+        // read-ahead stays inside the padded offsets (-inf rows).
+        constexpr int U = SCAN_U;
+        auto gather = [&](const int2 (&m)[U], float (&a)[U], float (&c)[U]) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                a[u] = *reinterpret_cast<const float *>(scl + m[u].x);
+                if constexpr (P == 2) c[u] = *reinterpret_cast<const float *>(scl + m[u].y);
+            }
+        };
         int n = 0;
-        for (; n + U <= last + 1; n += U) {
+        if (U <= last + 1) {
             int2 m[U];
-            float sg[U];
+            float a0[U], c0[U], a1[U], c1[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) m[u] = meta_s[n + u];
+            for (int u = 0; u < U; ++u) m[u] = meta_s[u];
+            gather(m, a0, c0);
 #pragma unroll
-            for (int u = 0; u < U; ++u) sg[u] = sigma(m[u]);
+            for (int u = 0; u < U; ++u) m[u] = meta_s[U + u];
+            // two batches per trip, so the buffers alternate without copies
+            while (true) {
+                gather(m, a1, c1);                              // batch n + U
 #pragma unroll
-            for (int u = 0; u < U; ++u) visit(sg[u], n + u);
+                for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) visit(P == 1 ? a0[u] : a0[u] + c0[u], n + u);
+                __builtin_amdgcn_sched_barrier(0);
+                n += U;
+                if (n + U > last + 1) break;
+                gather(m, a0, c0);                              // batch n + U
+#pragma unroll
+                for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < U; ++u) visit(P == 1 ? a1[u] : a1[u] + c1[u], n + u);
+                __builtin_amdgcn_sched_barrier(0);
+                n += U;
+                if (n + U > last + 1) break;
+            }
         }
         for (; n <= last; ++n) visit(sigma(meta_s[n]), n);
     }
     // address of an indexed block, from its score-row offsets
     auto addr_of = [&](int nn) {
         const int2 m = meta_s[nn];
-        const int c0 = m.x / (WAVE * 4);
-        return P == 1 ? c0 : c0 * K + (m.y / (WAVE * 4) - K);
+        const int c0 = m.x / (SROW * 4);
+        return P == 1 ? c0 : c0 * K + (m.y / (SROW * 4) - K);
     };
     // does (sigma, address) rank after the n_probes-th address?
     auto after_tau = [&](float sg, int a) {
@@ -496,29 +727,35 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
     walk_ext(add);
 
     // ---- rerank: two candidates at a time, their summaries loaded together
-    // (indexes clamped so the loads of empty slots stay in bounds)
+    // (indexes clamped so the loads of empty slots stay in bounds).  A pool
+    // of at most R blocks is kept whole whatever its scores, so its lanes
+    // skip the summaries and insert their blocks with equal keys (they come
+    // out ascending either way).
+    const bool rr = nc > R;
 #pragma unroll
     for (int i = 0; i < MAXC; i += 2) {
         if (__ballot(i < nc) == 0ull) break;
         const int n0 = cand[i] >= 0 ? cand[i] : 0, n1 = cand[i + 1] >= 0 ? cand[i + 1] : 0;
-        const float *k0 = kb + (size_t)n0 * D, *k1 = kb + (size_t)n1 * D;
-        float4 v0[D / 4], v1[D / 4];
-#pragma unroll
-        for (int j = 0; j < D / 4; ++j) {
-            v0[j] = reinterpret_cast<const float4 *>(k0)[j];
-            v1[j] = reinterpret_cast<const float4 *>(k1)[j];
-        }
         float acc0 = 0.0f, acc1 = 0.0f;
+        if (rr && i < nc) {
+            const float *k0 = kb + (size_t)n0 * D, *k1 = kb + (size_t)n1 * D;
+            float4 v0[D / 4], v1[D / 4];
 #pragma unroll
-        for (int j = 0; j < D / 4; ++j) {
-            acc0 = __builtin_fmaf(qr[4 * j], v0[j].x, acc0);
-            acc0 = __builtin_fmaf(qr[4 * j + 1], v0[j].y, acc0);
-            acc0 = __builtin_fmaf(qr[4 * j + 2], v0[j].z, acc0);
-            acc0 = __builtin_fmaf(qr[4 * j + 3], v0[j].w, acc0);
-            acc1 = __builtin_fmaf(qr[4 * j], v1[j].x, acc1);
-            acc1 = __builtin_fmaf(qr[4 * j + 1], v1[j].y, acc1);
-            acc1 = __builtin_fmaf(qr[4 * j + 2], v1[j].z, acc1);
-            acc1 = __builtin_fmaf(qr[4 * j + 3], v1[j].w, acc1);
+            for (int j = 0; j < D / 4; ++j) {
+                v0[j] = reinterpret_cast<const float4 *>(k0)[j];
+                v1[j] = reinterpret_cast<const float4 *>(k1)[j];
+            }
+#pragma unroll
+            for (int j = 0; j < D / 4; ++j) {
+                acc0 = __builtin_fmaf(qr[4 * j], v0[j].x, acc0);
+                acc0 = __builtin_fmaf(qr[4 * j + 1], v0[j].y, acc0);
+                acc0 = __builtin_fmaf(qr[4 * j + 2], v0[j].z, acc0);
+                acc0 = __builtin_fmaf(qr[4 * j + 3], v0[j].w, acc0);
+                acc1 = __builtin_fmaf(qr[4 * j], v1[j].x, acc1);
+                acc1 = __builtin_fmaf(qr[4 * j + 1], v1[j].y, acc1);
+                acc1 = __builtin_fmaf(qr[4 * j + 2], v1[j].z, acc1);
+                acc1 = __builtin_fmaf(qr[4 * j + 3], v1[j].w, acc1);
+            }
         }
         if (i < nc) insert(rk, key_of(acc0, (uint32_t)(0x7FFFFFFF - n0)));
         if (i + 1 < nc) insert(rk, key_of(acc1, (uint32_t)(0x7FFFFFFF - n1)));
