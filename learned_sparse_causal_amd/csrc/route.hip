@@ -36,6 +36,8 @@
 // Ordered choices use 64-bit keys where a larger key is better: the high
 // word is the score mapped to an order-preserving unsigned integer, the low
 // word breaks ties toward the lower address / code / block.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace {
@@ -89,7 +91,8 @@ __host__ __device__ constexpr int route_wave_floats(int PK, int DS, bool mf) {
 constexpr int STAGE_OFF = 8, STAGE_BLK = STAGE_OFF / 2;
 
 template <int D, int P, int NPRM, int RM, bool BF16, bool MF>
-__global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && NPRM <= 8 ? 2 : 1))) void k_route(
+    Shape s, const void *__restrict__ q,
                                                const float *__restrict__ cos_t,
                                                const float *__restrict__ sin_t,
                                                const float *__restrict__ cb,
@@ -451,42 +454,83 @@ __global__ __launch_bounds__(256) void k_route(Shape s, const void *__restrict__
                 }
         }
         }
-        const int NT = (K + 15) / 16;
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
+        // Component p: the MFMA chains of both 16-code tiles (codes past K
+        // have zero columns and are not stored), then the stores into the
+        // score table.  With 32 codes the ranking of component 0 is
+        // straight-line code placed after component 1's chains are issued,
+        // so its VALU work fills the matrix pipe's time.
+        f32x4 acc[P][NTM][MT];
+        auto chains = [&](int p) {
 #pragma unroll
             for (int nt = 0; nt < NTM; ++nt) {
-                if (nt >= NT) break;
-                // B operand (loaded at the start): code nt*16 + lr, dimension
-                // 4 st + lg; columns past the last code are zero
                 const int code = nt * 16 + lr;
                 float bf[NS];
 #pragma unroll
                 for (int st = 0; st < NS; ++st) bf[st] = code < K ? bpre[p][nt][st] : 0.0f;
-                f32x4 acc[MT];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int mt = 0; mt < MT; ++mt) acc[p][nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int st = 0; st < NS; ++st)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[p][mt][st], bf[st],
-                                                                       acc[mt], 0, 0, 0);
+                        acc[p][nt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            af[p][mt][st], bf[st], acc[p][nt][mt], 0, 0, 0);
+            }
+        };
+        auto store = [&](int p, auto all_codes) {
+#pragma unroll
+            for (int nt = 0; nt < NTM; ++nt) {
                 // lane holds routes mt*16 + 4 lg + r of code nt*16 + lr
-                if (code < K) {
+                const int code = nt * 16 + lr;
+                if (decltype(all_codes)::value || code < K) {
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
                         *reinterpret_cast<float4 *>(sc_s + (p * K + code) * SROW + mt * 16 + 4 * lg) =
-                            make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+                            make_float4(acc[p][nt][mt][0], acc[p][nt][mt][1], acc[p][nt][mt][2],
+                                        acc[p][nt][mt][3]);
                 }
             }
-        }
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
+        };
+        auto rank_codes = [&](int p, auto kc) {
 #pragma unroll
             for (int x = 0; x < NPRM; ++x) { tv[p][x] = -INFINITY; tc[p][x] = -1; }
+            if constexpr (decltype(kc)::value > 0) {
+#pragma unroll
+                for (int c = 0; c < decltype(kc)::value; ++c)
+                    top_insert(tv[p], tc[p], sc_s[(p * K + c) * SROW + lane], c);
+            } else {
 #pragma unroll 4
-            for (int c = 0; c < K; ++c) top_insert(tv[p], tc[p], sc_s[(p * K + c) * SROW + lane], c);
+                for (int c = 0; c < K; ++c) top_insert(tv[p], tc[p], sc_s[(p * K + c) * SROW + lane], c);
+            }
+        };
+        using all_codes = std::integral_constant<bool, true>;
+        using some_codes = std::integral_constant<bool, false>;
+        chains(0);
+        if (P == 2 && K == 32) {
+            store(0, all_codes{});
+            __builtin_amdgcn_wave_barrier();
+            chains(P - 1);
+            rank_codes(0, std::integral_constant<int, 32>{});
+            // one MFMA, then a score read and seven ranking instructions
+#pragma unroll
+            for (int i = 0; i < NTM * MT * NS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+            }
+            store(P - 1, all_codes{});
+            __builtin_amdgcn_wave_barrier();
+            rank_codes(P - 1, std::integral_constant<int, 32>{});
+        } else {
+            store(0, some_codes{});
+#pragma unroll
+            for (int p = 1; p < P; ++p) {
+                chains(p);
+                store(p, some_codes{});
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int p = 0; p < P; ++p) rank_codes(p, std::integral_constant<int, 0>{});
         }
     } else {
     const float *cbg = cb + (size_t)g * PK * DS;
