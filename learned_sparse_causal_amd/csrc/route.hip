@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         };
         // Software pipeline over batches of U blocks: the row offsets are
         // loaded two batches ahead and the score gathers one batch ahead,
-        // so the visits of a batch overlap the next batch's LDS reads.  The
+        // so the work on a batch overlaps the next batch's LDS reads.  The
         // read-ahead stays inside the padded offsets (-inf rows).
         constexpr int U = SCAN_U;
         auto gather = [&](const int2 (&m)[U], float (&a)[U], float (&c)[U]) {
@@ -701,6 +701,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
                 a[u] = *reinterpret_cast<const float *>(scl + m[u].x);
                 if constexpr (P == 2) c[u] = *reinterpret_cast<const float *>(scl + m[u].y);
             }
+        };
+        // Two slots: the scan keeps the two values only (slot 1 takes the
+        // median of old slot 0, old slot 1 and the new sigma; slot 0 the
+        // larger), plus the batch each slot's block came from: a batch that
+        // raises slot 0 gives it its first block of that sigma; slot 1 then
+        // holds the batch's runner-up or the old slot 0.  The block ids are
+        // recovered afterwards from those two batches.
+        float v0 = bs[0], v1 = bs[RM - 1];
+        int bb0 = -1, bb1 = -1;
+        auto batch_vals = [&](const float (&sg)[U], int batch) {
+            float n0 = v0, n1 = v1;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool b = sg[u] > n0;
+                n1 = __builtin_amdgcn_fmed3f(n0, n1, sg[u]);
+                n0 = b ? sg[u] : n0;
+            }
+            const bool up0 = n0 > v0;
+            bb1 = up0 ? (n1 > v0 ? batch : bb0) : (n1 > v1 ? batch : bb1);
+            bb0 = up0 ? batch : bb0;
+            v0 = n0;
+            v1 = n1;
         };
         int n = 0;
         if (U <= last + 1) {
@@ -717,8 +739,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 #pragma unroll
                 for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (RM == 2) {
+                    float sg[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) visit(P == 1 ? a0[u] : a0[u] + c0[u], n + u);
+                    for (int u = 0; u < U; ++u) sg[u] = P == 1 ? a0[u] : a0[u] + c0[u];
+                    batch_vals(sg, n / U);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) visit(P == 1 ? a0[u] : a0[u] + c0[u], n + u);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 n += U;
                 if (n + U > last + 1) break;
@@ -726,14 +755,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 #pragma unroll
                 for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (RM == 2) {
+                    float sg[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) visit(P == 1 ? a1[u] : a1[u] + c1[u], n + u);
+                    for (int u = 0; u < U; ++u) sg[u] = P == 1 ? a1[u] : a1[u] + c1[u];
+                    batch_vals(sg, n / U);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) visit(P == 1 ? a1[u] : a1[u] + c1[u], n + u);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 n += U;
                 if (n + U > last + 1) break;
             }
         }
-        for (; n <= last; ++n) visit(sigma(meta_s[n]), n);
+        if constexpr (RM == 2) {
+            // the partial last batch (its padded read-ahead rows are -inf)
+            if (n <= last) {
+                float sg[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float v = sigma(meta_s[n + u]);
+                    sg[u] = n + u <= last ? v : -INFINITY;
+                }
+                batch_vals(sg, n / U);
+            }
+            // the first block of a batch whose sigma equals val, other than excl
+            auto find = [&](int batch, float val, int excl) {
+                int res = -1;
+                if (batch >= 0) {
+#pragma unroll
+                    for (int u = U - 1; u >= 0; --u) {
+                        const int nn = batch * U + u;
+                        const bool hit = nn <= last && nn != excl && sigma(meta_s[nn]) == val;
+                        res = hit ? nn : res;
+                    }
+                }
+                return res;
+            };
+            bn[0] = RM - R == 0 && v0 > -INFINITY ? find(bb0, v0, -1) : -1;
+            bn[1] = v1 > -INFINITY ? find(bb1, v1, bn[0]) : -1;
+            bs[0] = v0;
+            bs[1] = v1;
+        } else {
+            for (; n <= last; ++n) visit(sigma(meta_s[n]), n);
+        }
     }
     // address of an indexed block, from its score-row offsets
     auto addr_of = [&](int nn) {
