@@ -200,6 +200,61 @@ struct VtStager {
     }
 };
 
+// V^T tile stager for bf16 (256 threads): each task takes 4 consecutive
+// keys x 4 dims (four 8-byte loads) and writes, per dim, the 4 keys as one
+// 8-byte LDS store.  The 4-key granules of dim row r are stored XOR-swizzled
+// by 2 (r / 16), i.e. key column x of row r sits at x ^ (8 (r / 16)): the
+// stores of a half-wave (16 dim chunks x 2 quads, or 32 chunks x 1 quad)
+// then fall on distinct banks, while a fragment read (16 rows of one 16-row
+// block) sees one XOR for all its lanes.
+template <int D>
+struct VtStagerPacked {
+    static constexpr int NC = D / 4;                // 4-dim chunks per key row
+    static constexpr int PER = 16 * NC / 256;       // tasks per thread
+    uint2 v[PER][4];
+    __device__ __forceinline__ void issue(const u16 *src, size_t row0, size_t stride) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int task = threadIdx.x + p * 256;
+            const int c = task % NC, j = task / NC;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[p][i] = *reinterpret_cast<const uint2 *>(src + row0 + (size_t)(4 * j + i) * stride +
+                                                           4 * c);
+        }
+    }
+    __device__ __forceinline__ void commit(u16 *dst) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int task = threadIdx.x + p * 256;
+            const int c = task % NC, j = task / NC;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t x = e < 2 ? v[p][i].x : v[p][i].y;
+                    w[i] = (e & 1) ? x >> 16 : x & 0xFFFFu;
+                }
+                const int row = 4 * c + e;
+                *reinterpret_cast<uint2 *>(dst + row * Tile<D, true>::VS +
+                                           ((4 * j) ^ (8 * (row >> 4)))) =
+                    make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+            }
+        }
+    }
+};
+
+// The V^T stager of a dtype: packed and swizzled for bf16, plain for fp32.
+template <int D, bool BF16>
+struct VtStagerOf {
+    using type = VtStager<D, BF16>;
+};
+template <int D>
+struct VtStagerOf<D, true> {
+    using type = VtStagerPacked<D>;
+};
+
 // The wave's Q^T fragments for one query row per lane (row offset `off`
 // elements, all-zero if !ok): dims 32c + 8(l/16) .. +7 for c < D/32.
 template <int D, bool BF16>
@@ -304,8 +359,11 @@ __device__ __forceinline__ void attend64(const Frag8<BF16> (&qf)[D / 32], const 
         const Frag8<BF16> pf = reg_frag8<BF16>(pv);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-            const Elem<BF16> *vr = Vt + (dt * 16 + lr) * T::VS + 32 * c + 4 * lg;
-            const Frag8<BF16> vf = lds_frag4x2(vr, vr + 16);
+            // bf16 V^T tiles are stored swizzled (VtStagerPacked)
+            const int sw = BF16 ? 8 * dt : 0;
+            const Elem<BF16> *vr = Vt + (dt * 16 + lr) * T::VS;
+            const Frag8<BF16> vf = lds_frag4x2(vr + ((32 * c + 4 * lg) ^ sw),
+                                               vr + ((32 * c + 16 + 4 * lg) ^ sw));
             mma32(o[dt], vf, pf);
         }
     }
@@ -616,7 +674,7 @@ __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *
         return (d.x >= 0 && row < d.z) ? row : -1;
     };
     RowStager<D, BF16> ks[NSUB];
-    VtStager<D, BF16> vs[NSUB];
+    typename VtStagerOf<D, BF16>::type vs[NSUB];
     auto kv_issue = [&](int bin) {
         const int n = bin % NB, g = (bin / NB) % Hkv, b = bin / (NB * Hkv);
 #pragma unroll
@@ -826,7 +884,7 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     int j = 0, sub = 0;
     if (nblk > 0 && item_key0(0, 0) < 0) next_item(j, sub);
     RowStager<D, BF16> kst;
-    VtStager<D, BF16> vst;
+    typename VtStagerOf<D, BF16>::type vst;
     auto issue_kv = [&](int kb0) {
         kst.issue(k_rot, [&](int r, size_t &off) {
             off = (((size_t)b * T_ + kb0 + r) * Hkv + g) * D;
@@ -1087,60 +1145,6 @@ __device__ __forceinline__ void dense_tile(const Frag8<BF16> (&qf)[NG][D / 32],
     }
 }
 
-// V^T tile stager for bf16 (256 threads): each task takes 4 consecutive
-// keys x 4 dims (four 8-byte loads) and writes, per dim, the 4 keys as one
-// 8-byte LDS store.  The 4-key granules of dim row r are stored XOR-swizzled
-// by 2 (r / 16), i.e. key column x of row r sits at x ^ (8 (r / 16)): the
-// stores of a half-wave (16 dim chunks x 2 quads, or 32 chunks x 1 quad)
-// then fall on distinct banks, while a fragment read (16 rows of one 16-row
-// block) sees one XOR for all its lanes.
-template <int D>
-struct VtStagerPacked {
-    static constexpr int NC = D / 4;                // 4-dim chunks per key row
-    static constexpr int PER = 16 * NC / 256;       // tasks per thread
-    uint2 v[PER][4];
-    __device__ __forceinline__ void issue(const u16 *src, size_t row0, size_t stride) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int task = threadIdx.x + p * 256;
-            const int c = task % NC, j = task / NC;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v[p][i] = *reinterpret_cast<const uint2 *>(src + row0 + (size_t)(4 * j + i) * stride +
-                                                           4 * c);
-        }
-    }
-    __device__ __forceinline__ void commit(u16 *dst) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int task = threadIdx.x + p * 256;
-            const int c = task % NC, j = task / NC;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t x = e < 2 ? v[p][i].x : v[p][i].y;
-                    w[i] = (e & 1) ? x >> 16 : x & 0xFFFFu;
-                }
-                const int row = 4 * c + e;
-                *reinterpret_cast<uint2 *>(dst + row * Tile<D, true>::VS +
-                                           ((4 * j) ^ (8 * (row >> 4)))) =
-                    make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
-            }
-        }
-    }
-};
-
-template <int D, bool BF16>
-struct DenseVt {
-    using type = VtStager<D, BF16>;
-};
-template <int D>
-struct DenseVt<D, true> {
-    using type = VtStagerPacked<D>;
-};
-
 constexpr int DENSE_NG = 2;                      // 16-query groups per wave
 constexpr int DENSE_ROWS = 4 * 16 * DENSE_NG;    // queries per workgroup (4 waves)
 
@@ -1189,7 +1193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
         qst[gi].issue(q_rot, (((size_t)b * T_ + qlim[gi]) * Hq + h) * D, wave_rows);
     }
     RowStager<D, BF16> kst;
-    typename DenseVt<D, BF16>::type vst;
+    typename VtStagerOf<D, BF16>::type vst;
     auto issue_kv = [&](int kt) {
         const int kb0 = kt * 64;
         kst.issue(k_rot, [&](int r, size_t &off) {
