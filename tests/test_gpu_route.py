@@ -40,7 +40,9 @@ CFGS = [configs.TINY, configs.SMALL, configs.ALL_ELIGIBLE, configs.sweep(4096),
         configs.SMALL.with_(name="cap1", cap=1, Hq=4, Hkv=4),
         # 65 blocks: the last route workgroup holds one wave of tokens
         configs.SMALL.with_(name="ragged_T4160_B2", T=4160, B=2, Hq=4, Hkv=2),
-        configs.SMALL.with_(name="gqa4_T3136_L3_R3", T=3136, Hq=8, Hkv=2, L=3, R=3, n_probes=3)]
+        configs.SMALL.with_(name="gqa4_T3136_L3_R3", T=3136, Hq=8, Hkv=2, L=3, R=3, n_probes=3),
+        # 4096 addresses: the list offsets take several staging rounds
+        configs.SMALL.with_(name="K64_P2_A4096", K=64, Hq=2, Hkv=2)]
 
 
 @pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
