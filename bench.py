@@ -12,12 +12,15 @@ floors, the 4K-32K sweep exponent, the routed step against the dense causal
 attention kernel (mono_dense_attention) at 4K-64K tokens, one decode step
 (mono_decode_step) and index update (mono_decode_index) on the batch-8
 64K-token cache, spherical codebook calibration (mono_calibrate_codebooks) on
-the 8192-token capacity workload with held-out overflow before and after, and
-the CPU oracle timed on the host cores.
+the 8192-token capacity workload with held-out overflow before and after,
+peaks measured on the GPU (a 1 GiB device copy, a library bf16 GEMM) with the
+path's roofline fraction against them, and the CPU oracle timed on the host
+cores (plus its index build and route alone on 4 threads over the sweep, with
+their exponent).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-dense]
                     [--dense-sizes 4096,...] [--no-decode] [--no-calibration]
-                    [--no-cpu-baseline] [--copy-calibration]
+                    [--no-onbox-peaks] [--no-cpu-baseline] [--copy-calibration]
 
 --copy-calibration runs a plain 256 MiB device copy before the steps; hardware
 counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -312,10 +315,66 @@ def cpu_baseline(cfg, reps=3):
         oracle.attention(sh, inp["q"], inp["k"], inp["v"], c, s, sel, None, threads)
         times.append(time.perf_counter() - t0)
     t_step = float(np.median(times))
+    # the index build and the route alone on 4 threads over the 4K-32K sweep
+    # (the configuration the pages time their build and search on), with the
+    # least-squares exponent of ln t on ln T
+    from learned_sparse_causal_amd import configs
+    pts = {}
+    for T in configs.SWEEP_T:
+        c4 = configs.sweep(T)
+        inp4 = synth.qkv(c4)
+        cc, ss = oracle.rope_table(c4.T, c4.d)
+        sh4 = oracle.Shape.of(**c4.shape_kw())
+        t0 = time.perf_counter()
+        idx = oracle.build_index(sh4, inp4["k"], cc, ss, inp4["codebooks"], 4)
+        oracle.route(sh4, inp4["q"], cc, ss, inp4["codebooks"], idx, None, 4)
+        pts[T] = time.perf_counter() - t0
+    ts = sorted(pts)
+    expo = float(np.polyfit(np.log(ts), np.log([pts[T] for T in ts]), 1)[0])
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=cfg.B * cfg.T / t_step, unit="tokens/s", cores=threads, kind="oracle",
                 sample="the whole step (index build, route and fp64 attention of all %d queries, "
                        "numpy-drawn inputs of the same distribution), %d runs, median %.2f s"
-                       % (cfg.routes, reps, t_step))
+                       % (cfg.routes, reps, t_step),
+                cpu_model=model, host_cpus=os.cpu_count(),
+                build_route_4_threads=dict(seconds={str(T): pts[T] for T in ts}, exponent=expo))
+
+
+def onbox_peaks():
+    """Peaks measured on this GPU: a device-to-device copy of 1 GiB (read +
+    write bytes / time) and a library bf16 GEMM (8192^3, torch.matmul)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    t_gemm = timed(lambda: torch.matmul(a, b), 5)
+    out = dict(hbm_copy_GBs=2 * n / t_copy / 1e9, bf16_gemm_TFLOPs=2 * 8192 ** 3 / t_gemm / 1e12)
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -329,6 +388,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
+    ap.add_argument("--no-onbox-peaks", action="store_true")
     ap.add_argument("--dense-sizes", default="4096,8192,16384,32768,65536",
                     help="token counts of the routed-vs-dense comparison")
     args = ap.parse_args()
@@ -408,6 +468,17 @@ def main():
         line["decode"] = run_decode(configs.LARGE)
     if not args.no_calibration:
         line["calibration"] = run_calibration(configs.ALL_ELIGIBLE)
+    if not args.no_onbox_peaks:
+        peaks = onbox_peaks()
+        f_box = {
+            "build": w["build_bytes"] / (peaks["hbm_copy_GBs"] * 1e9),
+            "route": max(w["route_bytes"] / (peaks["hbm_copy_GBs"] * 1e9),
+                         w["route_flops"] / (FP32_VECTOR_TFLOPS * 1e12)),
+            "attend": max(w["attn_bytes"] / (peaks["hbm_copy_GBs"] * 1e9),
+                          w["attn_flops"] / (peaks["bf16_gemm_TFLOPs"] * 1e12)),
+        }
+        peaks["path_roofline_frac"] = sum(f_box.values()) / (wall_ms * 1e-3)
+        line["onbox_peaks"] = peaks
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)
