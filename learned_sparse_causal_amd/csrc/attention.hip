@@ -766,7 +766,8 @@ __global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *
 }
 
 template <int D, int BETA, bool BF16>
-__global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1))) void k_attn_local(
+    Shape s, const Elem<BF16> *__restrict__ q_rot,
                                                     const Elem<BF16> *__restrict__ k_rot,
                                                     const Elem<BF16> *__restrict__ v,
                                                     const int32_t *__restrict__ sel,
@@ -801,6 +802,7 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     // log-sum-exps and partial rows when its attention is done.  (Prep
     // leaves every slot of a uniform tile at -1, so no tile flag is needed.)
     constexpr int RP = 2;
+    constexpr int RX = 6;   // further slots merged from registers (R <= RP + RX)
     int ep_c[RP], ep_n[RP];
     float lse_c[RP], lse_n[RP];
     PartChunks<D, BF16> o_c[RP], o_n[RP];
@@ -937,7 +939,68 @@ __global__ __launch_bounds__(256) void k_attn_local(Shape s, const Elem<BF16> *_
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[dt][r] = o[dt][r] * inv;
-    if (!uni) {
+    if (!uni && R > RP && R <= RP + RX) {
+        // slots RP .. R-1 come from global memory: their entry positions in
+        // one batch, then their log-sum-exps in one batch, then the partial
+        // rows two at a time (loads clamped to entry 0, weights of absent
+        // slots zero), accumulated in slot order
+        const int32_t *ep = entry_pos + route * R;
+        int ex[RX];
+        float lx[RX];
+#pragma unroll
+        for (int x = 0; x < RX; ++x) ex[x] = RP + x < R ? ep[RP + x] : -1;
+#pragma unroll
+        for (int x = 0; x < RX; ++x) lx[x] = part_lse[max(ex[x], 0)];
+        float M = lse;
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+            if (r < R && ep_c[r] >= 0) M = fmaxf(M, lse_c[r]);
+#pragma unroll
+        for (int x = 0; x < RX; ++x)
+            if (ex[x] >= 0) M = fmaxf(M, lx[x]);
+        float wsum = __builtin_amdgcn_exp2f(lse - M);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[dt][r] *= wsum;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {   // prefetched slots (static indexes)
+            if (r >= R || ep_c[r] < 0) continue;
+            const float w = __builtin_amdgcn_exp2f(lse_c[r] - M);
+            wsum += w;
+            float x[D / 16][4];
+            o_c[r].unpack(x);
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
+        }
+#pragma unroll
+        for (int x0 = 0; x0 < RX; x0 += 2) {
+            if (__ballot(ex[x0] >= 0 || (x0 + 1 < RX && ex[x0 + 1] >= 0)) == 0ull) continue;
+            PartChunks<D, BF16> pc[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (x0 + u < RX) pc[u].load(part_o + (size_t)max(ex[x0 + u], 0) * D, lg);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (x0 + u >= RX || ex[x0 + u] < 0) continue;
+                const float w = __builtin_amdgcn_exp2f(lx[x0 + u] - M);
+                wsum += w;
+                float x[D / 16][4];
+                pc[u].unpack(x);
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
+            }
+        }
+        const float iw = 1.0f / wsum;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[dt][r] *= iw;
+    } else if (!uni) {
         const int32_t *ep = entry_pos + route * R;
         auto ep_at = [&](int r) { return r < RP ? ep_c[r] : ep[r]; };
         auto lse_at = [&](int r) { return r < RP ? lse_c[r] : part_lse[ep[r]]; };
