@@ -647,7 +647,8 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
 // task computes.  The next chunk's K / V^T (if its bin differs) is staged in
 // registers during the current chunk and written to LDS after it.
 template <int D, int BETA, bool BF16>
-__global__ __launch_bounds__(256) void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1))) void k_attn_remote(
+    Shape s, const Elem<BF16> *__restrict__ q_rot,
                                                      const Elem<BF16> *__restrict__ k_rot,
                                                      const Elem<BF16> *__restrict__ v,
                                                      const int32_t *__restrict__ list_q,
