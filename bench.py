@@ -13,14 +13,16 @@ attention kernel (mono_dense_attention) at 4K-64K tokens, one decode step
 (mono_decode_step) and index update (mono_decode_index) on the batch-8
 64K-token cache, spherical codebook calibration (mono_calibrate_codebooks) on
 the 8192-token capacity workload with held-out overflow before and after,
-peaks measured on the GPU (a 1 GiB device copy, a library bf16 GEMM) with the
-path's roofline fraction against them, and the CPU oracle timed on the host
-cores (plus its index build and route alone on 4 threads over the sweep, with
-their exponent).
+the whole step on the batch-8 64K-token workload (d 128, R 8) with its overflow
+and maximum list load, peaks measured on the GPU (a 1 GiB device copy, a
+library bf16 GEMM) with the path's roofline fraction against them, and the CPU
+oracle timed on the host cores (plus its index build and route alone on 4
+threads over the sweep, with their exponent).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-sweep] [--no-dense]
                     [--dense-sizes 4096,...] [--no-decode] [--no-calibration]
-                    [--no-onbox-peaks] [--no-cpu-baseline] [--copy-calibration]
+                    [--no-onbox-peaks] [--no-large] [--no-cpu-baseline]
+                    [--copy-calibration]
 
 --copy-calibration runs a plain 256 MiB device copy before the steps; hardware
 counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -389,6 +391,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--no-onbox-peaks", action="store_true")
+    ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--dense-sizes", default="4096,8192,16384,32768,65536",
                     help="token counts of the routed-vs-dense comparison")
     args = ap.parse_args()
@@ -464,6 +467,28 @@ def main():
                                dense_mfma_frac=dense_flops(c) / (dms * 1e-3) / 1e12 /
                                BF16_MFMA_TFLOPS)
         line["dense_vs_routed"] = pts
+    if not args.no_large:
+        # the whole step on the largest workload (batch 8, 64K tokens, d 128,
+        # R 8), 1 warm-up + 3 timed steps, with its index statistics
+        c5 = configs.LARGE
+        _, st5, _, stats5, sel5 = run_gpu(c5, 3, 1, route_events=False)
+        w5 = workload_bytes_flops(c5, sel5.cpu().numpy())
+        del sel5
+        f5 = {
+            "build": w5["build_bytes"] / (HBM_PEAK_GBS * 1e9),
+            "route": max(w5["route_bytes"] / (HBM_PEAK_GBS * 1e9),
+                         w5["route_flops"] / (FP32_VECTOR_TFLOPS * 1e12)),
+            "attend": max(w5["attn_bytes"] / (HBM_PEAK_GBS * 1e9),
+                          w5["attn_flops"] / (BF16_MFMA_TFLOPS * 1e12)),
+        }
+        t5 = st5["step_gpu_us"] * 1e-6
+        line["large"] = dict(
+            workload=c5.name, step_ms=t5 * 1e3, tokens_per_s=c5.B * c5.T / t5,
+            stage_us={k: st5[k] for k in ("build", "route", "attend")},
+            floors_us={k: v * 1e6 for k, v in f5.items()},
+            path_roofline_frac=sum(f5.values()) / t5,
+            attend_mfma_frac=w5["attn_flops"] / (st5["attend"] * 1e-6) / 1e12 / BF16_MFMA_TFLOPS,
+            index=stats5)
     if not args.no_decode:
         line["decode"] = run_decode(configs.LARGE)
     if not args.no_calibration:
