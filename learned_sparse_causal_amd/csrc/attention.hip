@@ -647,15 +647,14 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
 // task computes.  The next chunk's K / V^T (if its bin differs) is staged in
 // registers during the current chunk and written to LDS after it.
 template <int D, int BETA, bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1))) void k_attn_remote(
-    Shape s, const Elem<BF16> *__restrict__ q_rot,
-                                                     const Elem<BF16> *__restrict__ k_rot,
-                                                     const Elem<BF16> *__restrict__ v,
-                                                     const int32_t *__restrict__ list_q,
-                                                     const int4 *__restrict__ chunk_desc,
-                                                     const int32_t *__restrict__ wg_first,
-                                                     float *__restrict__ part_lse,
-                                                     Elem<BF16> *__restrict__ part_o) {
+// bf16: capped at 256 registers (two waves per SIMD; the d = 128 kernels
+// would otherwise take one)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
+void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
+                   const Elem<BF16> *__restrict__ k_rot, const Elem<BF16> *__restrict__ v,
+                   const int32_t *__restrict__ list_q, const int4 *__restrict__ chunk_desc,
+                   const int32_t *__restrict__ wg_first, float *__restrict__ part_lse,
+                   Elem<BF16> *__restrict__ part_o) {
     using T = Tile<D, BF16>;
     using E = Elem<BF16>;
     constexpr int NSUB = BETA / 64;
@@ -767,16 +766,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
 }
 
 template <int D, int BETA, bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1))) void k_attn_local(
-    Shape s, const Elem<BF16> *__restrict__ q_rot,
-                                                    const Elem<BF16> *__restrict__ k_rot,
-                                                    const Elem<BF16> *__restrict__ v,
-                                                    const int32_t *__restrict__ sel,
-                                                    const int32_t *__restrict__ tile_flag,
-                                                    const int32_t *__restrict__ entry_pos,
-                                                    const float *__restrict__ part_lse,
-                                                    const Elem<BF16> *__restrict__ part_o,
-                                                    Elem<BF16> *__restrict__ out) {
+// bf16: capped at 256 registers (two waves per SIMD; the d = 128 kernels
+// would otherwise take one)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 1)))
+void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
+                  const Elem<BF16> *__restrict__ k_rot, const Elem<BF16> *__restrict__ v,
+                  const int32_t *__restrict__ sel, const int32_t *__restrict__ tile_flag,
+                  const int32_t *__restrict__ entry_pos, const float *__restrict__ part_lse,
+                  const Elem<BF16> *__restrict__ part_o, Elem<BF16> *__restrict__ out) {
     using T = Tile<D, BF16>;
     using E = Elem<BF16>;
     extern __shared__ __align__(16) unsigned char smem[];

@@ -14,7 +14,9 @@
 // four waves share one (batch, kv-head): its list offsets, list entries and,
 // per indexed block, the score-table rows of its component codes are staged
 // in LDS once, so list walks and block scans never wait on global memory.
-// Codebook reads have wave-uniform addresses and go through scalar loads.
+// The VALU scoring path reads the codebook with wave-uniform addresses
+// (scalar loads); the matrix-core path loads its B operands per lane at the
+// start of the kernel.
 //
 //  1. If E = qb - L + 1 <= R the selection is 0..E-1 (bypass).
 //  2. Rotate the query (fp32, products rounded before the add), score every
@@ -90,18 +92,16 @@ __host__ __device__ constexpr int route_wave_floats(int PK, int DS, bool mf) {
 // half as many blocks).
 constexpr int STAGE_OFF = 8, STAGE_BLK = STAGE_OFF / 2;
 
+// d = 64 with at most 8 probes fits 256 registers (two waves per SIMD, the
+// most the LDS allows); without the cap the compiler spends AGPRs on the
+// matrix-core accumulators and drops to one.
 template <int D, int P, int NPRM, int RM, bool BF16, bool MF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && NPRM <= 8 ? 2 : 1))) void k_route(
-    Shape s, const void *__restrict__ q,
-                                               const float *__restrict__ cos_t,
-                                               const float *__restrict__ sin_t,
-                                               const float *__restrict__ cb,
-                                               const float *__restrict__ kbar,
-                                               const int32_t *__restrict__ addr,
-                                               const int32_t *__restrict__ offsets,
-                                               const int32_t *__restrict__ entries,
-                                               int32_t *__restrict__ sel,
-                                               void *__restrict__ q_rot) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && NPRM <= 8 ? 2 : 1)))
+void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_t,
+             const float *__restrict__ sin_t, const float *__restrict__ cb,
+             const float *__restrict__ kbar, const int32_t *__restrict__ addr,
+             const int32_t *__restrict__ offsets, const int32_t *__restrict__ entries,
+             int32_t *__restrict__ sel, void *__restrict__ q_rot) {
     constexpr int H = D / 2;
     constexpr int DS = D / P;
     extern __shared__ float lds[];
