@@ -234,6 +234,7 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
     int32_t *hist = lds;            // [A] loads
     int32_t *off = lds + A;         // [A+1] list starts
     int32_t *run = lds + 2 * A + 1; // [A] blocks already placed per address
+    int32_t *adr = lds + 3 * A + 1; // [nbu] the addresses, for the ranking pass
     __shared__ int32_t part[PL_THREADS / WAVE];
     __shared__ int32_t ovf_s[PL_THREADS / WAVE];
 
@@ -242,7 +243,11 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
     const int tid = threadIdx.x;
     for (int a = tid; a < A; a += PL_THREADS) { hist[a] = 0; run[a] = 0; }
     __syncthreads();
-    for (int n = tid; n < nbu; n += PL_THREADS) atomicAdd(&hist[ad[n]], 1);
+    for (int n = tid; n < nbu; n += PL_THREADS) {
+        const int a = ad[n];
+        adr[n] = a;
+        atomicAdd(&hist[a], 1);
+    }
     __syncthreads();
 
     // exclusive scan of min(load, cap): each thread owns a contiguous chunk
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
         for (int c0 = 0; c0 < nbu; c0 += WAVE) {
             const int n = c0 + tid;
             const bool in = n < nbu;
-            const int a = in ? ad[n] : 0;
+            const int a = in ? adr[n] : 0;
             uint64_t m = __ballot(in);
             for (int bit = 0; bit < nbits; ++bit) {
                 const uint64_t bal = __ballot(in && ((a >> bit) & 1));
@@ -380,7 +385,9 @@ hipError_t launch_block_address(const Shape &s, const void *k, const float *cos_
 hipError_t launch_posting_lists_prefix(const Shape &s, int nbu, const int32_t *addr,
                                        int32_t *offsets, int32_t *entries, int32_t *load,
                                        int32_t *overflow, hipStream_t st) {
-    const size_t lds = (size_t)(3 * s.A + 1) * sizeof(int32_t);
+    const size_t lds = (size_t)(3 * s.A + 1 + nbu) * sizeof(int32_t);
+    const hipError_t e = mono_lds_limit(reinterpret_cast<const void *>(k_posting_lists), lds);
+    if (e != hipSuccess) return e;
     k_posting_lists<<<dim3(s.B * s.Hkv), PL_THREADS, lds, st>>>(s, nbu, addr, offsets, entries,
                                                                  load, overflow);
     return hipGetLastError();
