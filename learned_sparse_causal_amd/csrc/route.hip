@@ -92,11 +92,14 @@ __host__ __device__ constexpr int route_wave_floats(int PK, int DS, bool mf) {
 // half as many blocks).
 constexpr int STAGE_OFF = 8, STAGE_BLK = STAGE_OFF / 2;
 
-// d = 64 with at most 8 probes fits 256 registers (two waves per SIMD, the
-// most the LDS allows); without the cap the compiler spends AGPRs on the
-// matrix-core accumulators and drops to one.
+// At most 8 probes fits 256 registers (two waves per SIMD, the most the LDS
+// allows); without the cap the compiler spends AGPRs on the matrix-core
+// accumulators (d = 64) or on the rerank's summary loads (d = 128) and
+// drops to one.  At d = 128 the rerank loads the summaries in quarters so
+// that they fit beside the 128 registers of the rotated query, at the cost
+// of a few spilled registers on the path past the register batch.
 template <int D, int P, int NPRM, int RM, bool BF16, bool MF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && NPRM <= 8 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPRM <= 8 ? 2 : 1)))
 void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_t,
              const float *__restrict__ sin_t, const float *__restrict__ cb,
              const float *__restrict__ kbar, const int32_t *__restrict__ addr,
@@ -849,22 +852,29 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
         float acc0 = 0.0f, acc1 = 0.0f;
         if (rr && i < nc) {
             const float *k0 = kb + (size_t)n0 * D, *k1 = kb + (size_t)n1 * D;
-            float4 v0[D / 4], v1[D / 4];
+            constexpr int CH = D == 128 ? 8 : D / 4;   // float4 per candidate per round
 #pragma unroll
-            for (int j = 0; j < D / 4; ++j) {
-                v0[j] = reinterpret_cast<const float4 *>(k0)[j];
-                v1[j] = reinterpret_cast<const float4 *>(k1)[j];
-            }
+            for (int j0 = 0; j0 < D / 4; j0 += CH) {
+                float4 v0[CH], v1[CH];
 #pragma unroll
-            for (int j = 0; j < D / 4; ++j) {
-                acc0 = __builtin_fmaf(qr[4 * j], v0[j].x, acc0);
-                acc0 = __builtin_fmaf(qr[4 * j + 1], v0[j].y, acc0);
-                acc0 = __builtin_fmaf(qr[4 * j + 2], v0[j].z, acc0);
-                acc0 = __builtin_fmaf(qr[4 * j + 3], v0[j].w, acc0);
-                acc1 = __builtin_fmaf(qr[4 * j], v1[j].x, acc1);
-                acc1 = __builtin_fmaf(qr[4 * j + 1], v1[j].y, acc1);
-                acc1 = __builtin_fmaf(qr[4 * j + 2], v1[j].z, acc1);
-                acc1 = __builtin_fmaf(qr[4 * j + 3], v1[j].w, acc1);
+                for (int j = 0; j < CH; ++j) {
+                    v0[j] = reinterpret_cast<const float4 *>(k0)[j0 + j];
+                    v1[j] = reinterpret_cast<const float4 *>(k1)[j0 + j];
+                }
+#pragma unroll
+                for (int jj = 0; jj < CH; ++jj) {
+                    const int j = j0 + jj;
+                    acc0 = __builtin_fmaf(qr[4 * j], v0[jj].x, acc0);
+                    acc0 = __builtin_fmaf(qr[4 * j + 1], v0[jj].y, acc0);
+                    acc0 = __builtin_fmaf(qr[4 * j + 2], v0[jj].z, acc0);
+                    acc0 = __builtin_fmaf(qr[4 * j + 3], v0[jj].w, acc0);
+                    acc1 = __builtin_fmaf(qr[4 * j], v1[jj].x, acc1);
+                    acc1 = __builtin_fmaf(qr[4 * j + 1], v1[jj].y, acc1);
+                    acc1 = __builtin_fmaf(qr[4 * j + 2], v1[jj].z, acc1);
+                    acc1 = __builtin_fmaf(qr[4 * j + 3], v1[jj].w, acc1);
+                }
+                // keep the next quarter's loads behind this quarter's chains
+                if constexpr (CH < D / 4) __builtin_amdgcn_sched_barrier(0);
             }
         }
         if (i < nc) insert(rk, key_of(acc0, (uint32_t)(0x7FFFFFFF - n0)));
