@@ -656,20 +656,24 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
     int bn[RM];
 #pragma unroll
     for (int x = 0; x < RM; ++x) { bs[x] = x < RM - R ? INFINITY : -INFINITY; bn[x] = -1; }
+    // more than two slots: the R-th best sigma and the R-th best block
+    float vR = -INFINITY;
+    int nR = -1;
+    const char *scl = reinterpret_cast<const char *>(sc_s + lane);
+    auto sigma = [&](int2 m) {
+        const float a0 = *reinterpret_cast<const float *>(scl + m.x);
+        if constexpr (P == 1) return a0;
+        const float a1 = *reinterpret_cast<const float *>(scl + m.y);
+        return a0 + a1;
+    };
     if (__ballot(need) != 0ull) {
-        const char *scl = reinterpret_cast<const char *>(sc_s + lane);
-        auto sigma = [&](int2 m) {
-            const float a0 = *reinterpret_cast<const float *>(scl + m.x);
-            if constexpr (P == 1) return a0;
-            const float a1 = *reinterpret_cast<const float *>(scl + m.y);
-            return a0 + a1;
-        };
-        // The list is sorted and a new block's id exceeds every resident's,
-        // so only the new block is compared (strictly: a resident of equal
-        // sigma has the lower id); it takes the first slot it beats and the
-        // slots after it shift down by one.  Short lists are updated without
-        // a branch (lanes that need no extension update a list they never
-        // read).
+        // Two slots: the list is sorted and a new block's id exceeds every
+        // resident's, so only the new block is compared (strictly: a
+        // resident of equal sigma has the lower id).  More slots: the scan
+        // keeps the values only (slot x takes the median of old slots x - 1,
+        // x and the new sigma, slot 0 the larger of the two), and a second
+        // pass recovers the blocks.  Lanes that need no extension update
+        // lists they never read.
         auto visit = [&](float sg, int n) {
             if constexpr (RM == 2) {
                 // two slots: slot 1 takes the median of (slot 0, slot 1,
@@ -680,17 +684,11 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
                 bn[0] = b0 ? n : bn[0];
                 bs[1] = __builtin_amdgcn_fmed3f(bs[0], bs[1], sg);
                 bs[0] = b0 ? sg : bs[0];
-            } else if (RM <= 2 || (need & (sg > bs[RM - 1]))) {   // short lists: no branch
-                bool beat[RM];
+            } else {
+                (void)n;
 #pragma unroll
-                for (int x = 0; x < RM; ++x) beat[x] = sg > bs[x];
-#pragma unroll
-                for (int x = RM - 1; x > 0; --x) {
-                    bs[x] = beat[x] ? (beat[x - 1] ? bs[x - 1] : sg) : bs[x];
-                    bn[x] = beat[x] ? (beat[x - 1] ? bn[x - 1] : n) : bn[x];
-                }
-                bs[0] = beat[0] ? sg : bs[0];
-                bn[0] = beat[0] ? n : bn[0];
+                for (int x = RM - 1; x > 0; --x) bs[x] = __builtin_amdgcn_fmed3f(bs[x - 1], bs[x], sg);
+                bs[0] = sg > bs[0] ? sg : bs[0];
             }
         };
         // Software pipeline over batches of U blocks: the row offsets are
@@ -727,52 +725,48 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
             v0 = n0;
             v1 = n1;
         };
-        int n = 0;
-        if (U <= last + 1) {
-            int2 m[U];
-            float a0[U], c0[U], a1[U], c1[U];
+        // one pass over the blocks 0..last in batches of U: consume(sg, n0)
+        // gets the sigmas of blocks n0 .. n0 + U - 1 (-inf past last)
+        auto scan = [&](auto &&consume) {
+            int n = 0;
+            if (U <= last + 1) {
+                int2 m[U];
+                float a0[U], c0[U], a1[U], c1[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) m[u] = meta_s[u];
-            gather(m, a0, c0);
+                for (int u = 0; u < U; ++u) m[u] = meta_s[u];
+                gather(m, a0, c0);
 #pragma unroll
-            for (int u = 0; u < U; ++u) m[u] = meta_s[U + u];
-            // two batches per trip, so the buffers alternate without copies
-            while (true) {
-                gather(m, a1, c1);                              // batch n + U
+                for (int u = 0; u < U; ++u) m[u] = meta_s[U + u];
+                // two batches per trip, so the buffers alternate without copies
+                while (true) {
+                    gather(m, a1, c1);                              // batch n + U
 #pragma unroll
-                for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (RM == 2) {
-                    float sg[U];
+                    for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
+                    __builtin_amdgcn_sched_barrier(0);
+                    {
+                        float sg[U];
 #pragma unroll
-                    for (int u = 0; u < U; ++u) sg[u] = P == 1 ? a0[u] : a0[u] + c0[u];
-                    batch_vals(sg, n / U);
-                } else {
+                        for (int u = 0; u < U; ++u) sg[u] = P == 1 ? a0[u] : a0[u] + c0[u];
+                        consume(sg, n);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    n += U;
+                    if (n + U > last + 1) break;
+                    gather(m, a0, c0);                              // batch n + U
 #pragma unroll
-                    for (int u = 0; u < U; ++u) visit(P == 1 ? a0[u] : a0[u] + c0[u], n + u);
+                    for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
+                    __builtin_amdgcn_sched_barrier(0);
+                    {
+                        float sg[U];
+#pragma unroll
+                        for (int u = 0; u < U; ++u) sg[u] = P == 1 ? a1[u] : a1[u] + c1[u];
+                        consume(sg, n);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    n += U;
+                    if (n + U > last + 1) break;
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                n += U;
-                if (n + U > last + 1) break;
-                gather(m, a0, c0);                              // batch n + U
-#pragma unroll
-                for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (RM == 2) {
-                    float sg[U];
-#pragma unroll
-                    for (int u = 0; u < U; ++u) sg[u] = P == 1 ? a1[u] : a1[u] + c1[u];
-                    batch_vals(sg, n / U);
-                } else {
-#pragma unroll
-                    for (int u = 0; u < U; ++u) visit(P == 1 ? a1[u] : a1[u] + c1[u], n + u);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                n += U;
-                if (n + U > last + 1) break;
             }
-        }
-        if constexpr (RM == 2) {
             // the partial last batch (its padded read-ahead rows are -inf)
             if (n <= last) {
                 float sg[U];
@@ -781,8 +775,11 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
                     const float v = sigma(meta_s[n + u]);
                     sg[u] = n + u <= last ? v : -INFINITY;
                 }
-                batch_vals(sg, n / U);
+                consume(sg, n);
             }
+        };
+        if constexpr (RM == 2) {
+            scan([&](const float (&sg)[U], int n0) { batch_vals(sg, n0 / U); });
             // the first block of a batch whose sigma equals val, other than excl
             auto find = [&](int batch, float val, int excl) {
                 int res = -1;
@@ -801,7 +798,33 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
             bs[0] = v0;
             bs[1] = v1;
         } else {
-            for (; n <= last; ++n) visit(sigma(meta_s[n]), n);
+            scan([&](const float (&sg)[U], int n0) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) visit(sg[u], n0 + u);
+            });
+            // The R best are the blocks above the R-th value plus the first
+            // blocks (source order) equal to it, as many as slots hold that
+            // value; none if that value is -inf (fewer than R indexed
+            // blocks).  The second pass shifts them into bn (latest first)
+            // and keeps the last equal one: the R-th best block.  (Lanes
+            // that need no extension fill lists they never read.)
+            vR = bs[RM - 1];
+            int eq_left = 0;
+#pragma unroll
+            for (int x = 0; x < RM; ++x) eq_left += (x >= RM - R && bs[x] == vR) ? 1 : 0;
+            if (vR == -INFINITY) eq_left = 0;
+            scan([&](const float (&sg)[U], int n0) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool eq = (sg[u] == vR) & (eq_left > 0);
+                    const bool take = (sg[u] > vR) | eq;
+                    eq_left -= eq ? 1 : 0;
+                    nR = eq ? n0 + u : nR;
+#pragma unroll
+                    for (int x = RM - 1; x > 0; --x) bn[x] = take ? bn[x - 1] : bn[x];
+                    bn[0] = take ? n0 + u : bn[0];
+                }
+            });
         }
     }
     // address of an indexed block, from its score-row offsets
@@ -821,18 +844,24 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
         if (!need) return;
 #pragma unroll
         for (int x = 0; x < RM; ++x) {
-            if (x < RM - R || bn[x] < 0) continue;
-            if (after_tau(bs[x], addr_of(bn[x]))) fn(bn[x]);
+            if constexpr (RM == 2) {
+                if (x < RM - R || bn[x] < 0) continue;
+                if (after_tau(bs[x], addr_of(bn[x]))) fn(bn[x]);
+            } else {
+                if (bn[x] < 0) continue;
+                if (after_tau(sigma(meta_s[bn[x]]), addr_of(bn[x]))) fn(bn[x]);
+            }
         }
-        const int nR = bn[RM - 1];
-        if (nR >= 0) {
-            const int aR = addr_of(nR);
-            if (after_tau(bs[RM - 1], aR)) {
+        const int nR_ = RM == 2 ? bn[RM - 1] : nR;
+        const float vR_ = RM == 2 ? bs[RM - 1] : vR;
+        if (nR_ >= 0) {
+            const int aR = addr_of(nR_);
+            if (after_tau(vR_, aR)) {
                 const int e1 = off_s[aR + 1];
                 for (int e = off_s[aR]; e < e1; ++e) {
                     const int nn = ent_s[e];
                     if (nn > last) break;
-                    if (nn > nR) fn(nn);
+                    if (nn > nR_) fn(nn);
                 }
             }
         }
