@@ -42,7 +42,12 @@ CFGS = [configs.TINY, configs.SMALL, configs.ALL_ELIGIBLE, configs.sweep(4096),
         configs.SMALL.with_(name="ragged_T4160_B2", T=4160, B=2, Hq=4, Hkv=2),
         configs.SMALL.with_(name="gqa4_T3136_L3_R3", T=3136, Hq=8, Hkv=2, L=3, R=3, n_probes=3),
         # 4096 addresses: the list offsets take several staging rounds
-        configs.SMALL.with_(name="K64_P2_A4096", K=64, Hq=2, Hkv=2)]
+        configs.SMALL.with_(name="K64_P2_A4096", K=64, Hq=2, Hkv=2),
+        # R in 3..8: the two-pass extension scan, with overflowed (unindexed)
+        # eligible blocks, and at d 128 in bf16 with one component
+        configs.SMALL.with_(name="cap2_R6_probes6", cap=2, R=6, n_probes=6, Hq=2, Hkv=2),
+        configs.SMALL.with_(name="d128_bf16_P1_R5", d=128, P=1, K=32, Hq=2, Hkv=1,
+                            n_probes=5, R=5)]
 
 
 @pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
@@ -88,10 +93,11 @@ def test_route_parity_large_sampled(orc):
         n, len(ids), g_idx["overflow"].sum(), g_idx["load"].max()))
 
 
-def test_route_with_overflowed_eligible_blocks(orc):
+@pytest.mark.parametrize("R", [2, 5])
+def test_route_with_overflowed_eligible_blocks(orc, R):
     """Every block on one address, capacity 1: searched queries see one indexed
     block and pad the rest with -1; bypassed queries take every eligible block."""
-    cfg = configs.SMALL.with_(name="one_address_cap1", cap=1, R=2, L=1, Hq=2, Hkv=2)
+    cfg = configs.SMALL.with_(name="one_address_cap1_R%d" % R, cap=1, R=R, L=1, Hq=2, Hkv=2)
     say("[route] %s" % cfg.name)
     k, cb = synth.stress_keys(cfg, "one_address")
     inp = synth.qkv(cfg)
@@ -101,7 +107,23 @@ def test_route_with_overflowed_eligible_blocks(orc):
     assert np.array_equal(g_sel.reshape(-1, cfg.R), o_sel)
     t = np.arange(cfg.T)
     searched = (t // cfg.beta - cfg.L + 1) > cfg.R
-    assert (g_sel[:, :, searched] == np.array([0, -1])).all()
+    assert (g_sel[:, :, searched] == np.array([0] + [-1] * (R - 1))).all()
+
+
+def test_route_tied_extension(orc):
+    """Two hot addresses (blocks alternate between them), one probe, R 5:
+    the extension fills from blocks of equal sigma, which rank by block."""
+    cfg = configs.SMALL.with_(name="two_clusters_R5_probes1", n_probes=1, R=5, L=1, Hq=2,
+                              Hkv=2)
+    say("[route] %s" % cfg.name)
+    k, cb = synth.stress_keys(cfg, "two_clusters")
+    inp = synth.qkv(cfg)
+    g_idx, g_sel = run_gpu(cfg, dev(inp["q"], cfg.dtype), dev(k, cfg.dtype), cb)
+    o_idx, o_sel, gaps = run_oracle(orc, cfg, inp["q"], k, cb)
+    bad = compare_index(cfg, g_idx, o_idx, excuse=False)
+    check_sel_invariants(cfg, g_sel, g_idx)
+    n = compare_sel(cfg, g_sel, o_sel, gaps, bad)
+    say("  excused routes: %d of %d" % (n, cfg.routes))
 
 
 def test_route_deterministic():
