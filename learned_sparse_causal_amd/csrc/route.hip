@@ -31,7 +31,9 @@
 //     eligible block whose address key is <= max(tau, key_R), key_R being
 //     the key of the R-th best indexed eligible block.  Lanes whose first
 //     n_probes lists hold < R eligible blocks need key_R: the wave scans the
-//     eligible blocks once, keeping the R best block keys.
+//     eligible blocks, keeping the R best block keys (R <= 2: one pass over
+//     values plus the batches they came from; larger R: one pass over values
+//     and a second that collects the blocks).
 //  5. Rerank: rho = fp32 fma chain <q_rot, kbar_n> in dimension order; the
 //     R best by (rho desc, block asc) are kept and written ascending.
 //
