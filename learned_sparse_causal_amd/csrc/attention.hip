@@ -376,6 +376,10 @@ constexpr int CHUNK_ROWS = 256;
 
 constexpr int PREP_THREADS = 1024;
 
+// RMAX > 0: R <= RMAX, and a lane keeps its row of the selection in
+// registers (one load per slot; the duplicate checks compare registers).
+// RMAX = 0: any R, the row is re-read from memory.
+template <int RMAX>
 __global__ __launch_bounds__(PREP_THREADS) void k_attn_prep(Shape s, const int32_t *__restrict__ sel,
                                                    int32_t *__restrict__ cnt,
                                                    int32_t *__restrict__ entry_pos,
@@ -397,22 +401,41 @@ __global__ __launch_bounds__(PREP_THREADS) void k_attn_prep(Shape s, const int32
         const long route = route0 + lane;
         const int32_t *row = sel + route * R;
         const int32_t *row0 = sel + route0 * R;
-        bool same = true;
-        for (int r = 0; r < R; ++r) same = same && row[r] == row0[r];
-        const bool uni = __ballot(!same) == 0ull;
-        if (lane == 0) tile_flag[((long)b * Hq + h) * (T_ / 64) + t0 / 64] = uni ? 1 : 0;
         int32_t *ep = entry_pos + route * R;
-        for (int r = 0; r < R; ++r) {
-            const int id = row[r];
-            bool valid = !uni && id >= 0 && id <= last;
-            for (int r2 = 0; valid && r2 < r; ++r2) valid = row[r2] != id;
-            ep[r] = valid ? atomicAdd(&hist[id], 1) : -1;
+        if constexpr (RMAX > 0) {
+            int v[RMAX];
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) v[r] = r < R ? row[r] : -1;
+            bool same = true;
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) same = same && (r >= R || v[r] == row0[r]);
+            const bool uni = __ballot(!same) == 0ull;
+            if (lane == 0) tile_flag[((long)b * Hq + h) * (T_ / 64) + t0 / 64] = uni ? 1 : 0;
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) {
+                if (r < R) {   // wave-uniform
+                    bool valid = !uni && v[r] >= 0 && v[r] <= last;
+#pragma unroll
+                    for (int r2 = 0; r2 < r; ++r2) valid = valid && v[r2] != v[r];
+                    ep[r] = valid ? atomicAdd(&hist[v[r]], 1) : -1;
+                }
+            }
+        } else {
+            bool same = true;
+            for (int r = 0; r < R; ++r) same = same && row[r] == row0[r];
+            const bool uni = __ballot(!same) == 0ull;
+            if (lane == 0) tile_flag[((long)b * Hq + h) * (T_ / 64) + t0 / 64] = uni ? 1 : 0;
+            for (int r = 0; r < R; ++r) {
+                const int id = row[r];
+                bool valid = !uni && id >= 0 && id <= last;
+                for (int r2 = 0; valid && r2 < r; ++r2) valid = row[r2] != id;
+                ep[r] = valid ? atomicAdd(&hist[id], 1) : -1;
+            }
         }
     }
     __syncthreads();
     int32_t *cg = cnt + (((size_t)b * Hkv + g) * nseg + seg) * NB;   // [b, g][seg][n]
     for (int n = threadIdx.x; n < NB; n += blockDim.x) cg[n] = hist[n];
-
 }
 
 // Rotate every q and k row once into the activation dtype (grid-wide stream;
@@ -1387,10 +1410,12 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
                                                reinterpret_cast<E *>(w.q_rot),
                                                reinterpret_cast<E *>(w.k_rot));
     }
-    hipError_t err = ensure_lds(k_attn_prep, (size_t)s.NB * sizeof(int));
+    auto *prep = s.R <= 2 ? k_attn_prep<2> : s.R <= 8 ? k_attn_prep<8>
+                                           : s.R <= 16 ? k_attn_prep<16> : k_attn_prep<0>;
+    hipError_t err = ensure_lds(prep, (size_t)s.NB * sizeof(int));
     if (err != hipSuccess) return err;
-    k_attn_prep<<<dim3((unsigned)nseg, (unsigned)s.Hkv, (unsigned)s.B), PREP_THREADS,
-                  (size_t)s.NB * sizeof(int), st>>>(s, sel, w.cnt, w.entry_pos, w.tile_flag, nseg);
+    prep<<<dim3((unsigned)nseg, (unsigned)s.Hkv, (unsigned)s.B), PREP_THREADS,
+           (size_t)s.NB * sizeof(int), st>>>(s, sel, w.cnt, w.entry_pos, w.tile_flag, nseg);
     k_attn_binsum<<<dim3((unsigned)nwg), BIN_WG, 0, st>>>(nbins, nseg, s.NB, w.cnt, w.seg_rel,
                                                           w.bin_local, w.chunk_local, w.wg_sum);
     k_attn_scan<<<1, 1024, 0, st>>>(nwg, w.wg_sum);
