@@ -47,7 +47,9 @@ CFGS = [configs.TINY, configs.SMALL, configs.ALL_ELIGIBLE, configs.sweep(4096),
         # eligible blocks, and at d 128 in bf16 with one component
         configs.SMALL.with_(name="cap2_R6_probes6", cap=2, R=6, n_probes=6, Hq=2, Hkv=2),
         configs.SMALL.with_(name="d128_bf16_P1_R5", d=128, P=1, K=32, Hq=2, Hkv=1,
-                            n_probes=5, R=5)]
+                            n_probes=5, R=5),
+        # sixteen slots, five of them sentinels
+        configs.SMALL.with_(name="probes9_R11_L3", n_probes=9, R=11, L=3, Hq=2, Hkv=2)]
 
 
 @pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
