@@ -721,9 +721,12 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
                 n1 = __builtin_amdgcn_fmed3f(n0, n1, sg[u]);
                 n0 = b ? sg[u] : n0;
             }
-            const bool up0 = n0 > v0;
-            bb1 = up0 ? (n1 > v0 ? batch : bb0) : (n1 > v1 ? batch : bb1);
-            bb0 = up0 ? batch : bb0;
+            // both candidates first, then one select: a nested conditional
+            // compiles to a branch on the execution mask
+            const int up0 = -(int)(n0 > v0);
+            const int x1 = n1 > v0 ? batch : bb0, y1 = n1 > v1 ? batch : bb1;
+            bb1 = y1 + ((x1 - y1) & up0);
+            bb0 = bb0 + ((batch - bb0) & up0);
             v0 = n0;
             v1 = n1;
         };
