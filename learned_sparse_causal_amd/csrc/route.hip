@@ -717,9 +717,10 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
             float n0 = v0, n1 = v1;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool b = sg[u] > n0;
+                // slot 0 takes the larger value: the median with +inf (one
+                // instruction and no compare mask; equal values are equal)
                 n1 = __builtin_amdgcn_fmed3f(n0, n1, sg[u]);
-                n0 = b ? sg[u] : n0;
+                n0 = __builtin_amdgcn_fmed3f(n0, sg[u], INFINITY);
             }
             // both candidates first, then one select: a nested conditional
             // compiles to a branch on the execution mask
