@@ -676,22 +676,11 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
         // x and the new sigma, slot 0 the larger of the two), and a second
         // pass recovers the blocks.  Lanes that need no extension update
         // lists they never read.
-        auto visit = [&](float sg, int n) {
-            if constexpr (RM == 2) {
-                // two slots: slot 1 takes the median of (slot 0, slot 1,
-                // new); equal values keep the resident
-                const bool b0 = sg > bs[0], b1 = sg > bs[1];
-                const int n1 = b1 ? n : bn[1];
-                bn[1] = b0 ? bn[0] : n1;
-                bn[0] = b0 ? n : bn[0];
-                bs[1] = __builtin_amdgcn_fmed3f(bs[0], bs[1], sg);
-                bs[0] = b0 ? sg : bs[0];
-            } else {
-                (void)n;
+        // more slots, first pass: the values only
+        auto visit = [&](float sg) {
 #pragma unroll
-                for (int x = RM - 1; x > 0; --x) bs[x] = __builtin_amdgcn_fmed3f(bs[x - 1], bs[x], sg);
-                bs[0] = sg > bs[0] ? sg : bs[0];
-            }
+            for (int x = RM - 1; x > 0; --x) bs[x] = __builtin_amdgcn_fmed3f(bs[x - 1], bs[x], sg);
+            bs[0] = __builtin_amdgcn_fmed3f(bs[0], sg, INFINITY);
         };
         // Software pipeline over batches of U blocks: the row offsets are
         // loaded two batches ahead and the score gathers one batch ahead,
@@ -806,7 +795,7 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
         } else {
             scan([&](const float (&sg)[U], int n0) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) visit(sg[u], n0 + u);
+                for (int u = 0; u < U; ++u) visit(sg[u]);
             });
             // The R best are the blocks above the R-th value plus the first
             // blocks (source order) equal to it, as many as slots hold that
