@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 
 from learned_sparse_causal_amd import binding, configs, synth
-from parity import (BF16_RTOL, F32_ATOL, NEAR_TIE, compare_index, dev, host, index_to_host,
-                    say, small_inputs, torch)
+from parity import (BF16_RTOL, F32_ATOL, MAX_EXCUSED, NEAR_TIE, compare_index, dev, host,
+                    index_to_host, say, small_inputs, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,7 +99,9 @@ def oracle_rows(orc, cfg, inp, positions):
 def compare_decode(cfg, orc_idx, ids, o_sel, gaps, o_out, g_sel, g_out):
     """g_sel [n, R] and g_out [n, d] in the order of ids.  Routes whose GPU
     selection differs must be oracle near-ties (or belong to a (b, kv-head)
-    with a near-tie address); attention is compared where selections agree."""
+    with a near-tie address), and such excused routes stay below 0.01 % of
+    the rows compared, as for mono_route; attention is compared where
+    selections agree."""
     tie_bg = (orc_idx["gap"] < NEAR_TIE).any(-1).any(-1)       # [B, Hkv]
     diff = (g_sel != o_sel).any(-1)
     for i in np.nonzero(diff)[0]:
@@ -107,6 +109,7 @@ def compare_decode(cfg, orc_idx, ids, o_sel, gaps, o_out, g_sel, g_out):
         b, h = divmod(rid // cfg.T, cfg.Hq)
         assert gaps[i].min() < NEAR_TIE or tie_bg[b, h // cfg.G], \
             "route (b=%d h=%d t=%d): gpu %s oracle %s" % (b, h, rid % cfg.T, g_sel[i], o_sel[i])
+    assert diff.sum() <= MAX_EXCUSED * len(ids), "%d excused of %d rows" % (diff.sum(), len(ids))
     keep = ~diff
     err = np.abs(g_out[keep].astype(np.float64) - o_out[keep])
     if cfg.dtype == "f32":

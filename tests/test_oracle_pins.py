@@ -257,11 +257,19 @@ def rotate64(x, cos, sin):
     return np.concatenate([a * c - b * s, b * c + a * s], -1)
 
 
+def rel_gap(best, second):
+    """Relative gap of a decision: (best - runner-up) / max(|best|, |runner-up|, 1e-30)."""
+    return (best - second) / max(abs(best), abs(second), 1e-30)
+
+
 def dual_form_selection(cfg, q_row_rot, scores, idx, b, g, qb):
     """The selection written as a threshold on address rank (the dual of the
     walk): pool = indexed eligible blocks whose address rank is <= m, with
     m = max(n_probes, first rank where the eligible count reaches R) (or all
-    addresses); then the R best by rerank score.  Scores here are fp64."""
+    addresses); then the R best by rerank score.  Scores here are fp64.
+    Also returns the two decision gaps: the pool boundary (rank m against
+    rank m + 1; +inf when every address is probed) and the rerank boundary
+    (R-th kept against the best dropped; +inf when the pool holds <= R)."""
     K, P, A, R, L = cfg.K, cfg.P, cfg.A, cfg.R, cfg.L
     sig = np.zeros(A)
     for a in range(A):
@@ -277,19 +285,26 @@ def dual_form_selection(cfg, q_row_rot, scores, idx, b, g, qb):
                 elig.append((rank[a], int(n)))
     elig.sort()
     if len(elig) >= R:
-        m = max(cfg.n_probes, elig[R - 1][0])
+        m = min(max(cfg.n_probes, elig[R - 1][0]), A)
     else:
         m = A
     pool = [n for r, n in elig if r <= m]
     kbar = idx["kbar"][b, g].astype(np.float64)
     rho = {n: float(q_row_rot @ kbar[n]) for n in pool}
-    best = sorted(pool, key=lambda n: (-rho[n], n))[:R]
-    return sorted(best) + [-1] * (R - len(best))
+    ranked = sorted(pool, key=lambda n: (-rho[n], n))
+    best = ranked[:R]
+    gap_pool = math.inf if m >= A else rel_gap(sig[order[m - 1]], sig[order[m]])
+    gap_rerank = math.inf if len(pool) <= R else rel_gap(rho[ranked[R - 1]], rho[ranked[R]])
+    return sorted(best) + [-1] * (R - len(best)), (gap_pool, gap_rerank)
 
 
 @pytest.mark.parametrize("cfg_name,n_probes", [("tiny", None), ("small", None), ("small", 1),
                                                ("small_exhaustive", None)])
 def test_route_equals_dual_form_brute_force(orc, cfg_name, n_probes):
+    """The walk against its dual form, both selections and both decision
+    gaps.  The gaps are recomputed here from fp64 scores, so they are
+    compared loosely (the oracle takes them from its fp32 scores); a gap
+    taken at the wrong boundary, or not at all, is off by far more."""
     if cfg_name == "tiny":
         cfg = configs.TINY
     else:
@@ -303,6 +318,7 @@ def test_route_equals_dual_form_brute_force(orc, cfg_name, n_probes):
     ids = rng.choice(cfg.routes, size=min(cfg.routes, 300), replace=False)
     sel, gaps = orc.route(sh, inp["q"], cos, sin, inp["codebooks"], idx, ids)
     mism = 0
+    n_gaps = [0, 0]
     for i, rid in enumerate(ids):
         t = rid % cfg.T
         h = (rid // cfg.T) % cfg.Hq
@@ -310,17 +326,153 @@ def test_route_equals_dual_form_brute_force(orc, cfg_name, n_probes):
         g, qb = h // cfg.G, t // cfg.beta
         E = max(0, qb - cfg.L + 1)
         if E <= cfg.R:
-            want = list(range(E)) + [-1] * (cfg.R - E)
+            want, want_gaps = list(range(E)) + [-1] * (cfg.R - E), (math.inf, math.inf)
         else:
             qr = rotate64(inp["q"][b, t, h], cos[t], sin[t])
             ds = cfg.d // cfg.P
             scores = [qr[p * ds:(p + 1) * ds] @ inp["codebooks"][g, p, c].astype(np.float64)
                       for p in range(cfg.P) for c in range(cfg.K)]
-            want = dual_form_selection(cfg, qr, scores, idx, b, g, qb)
+            want, want_gaps = dual_form_selection(cfg, qr, scores, idx, b, g, qb)
+        for j in range(2):
+            got_g, want_g = gaps[i][j], want_gaps[j]
+            if math.isinf(want_g) or math.isinf(got_g):
+                assert got_g == want_g, (rid, j, got_g, want_g)
+            else:
+                assert abs(got_g - want_g) <= 1e-4 * max(1.0, abs(want_g)), (rid, j, got_g, want_g)
+                n_gaps[j] += 1
         if sel[i].tolist() != want:
             assert gaps[i].min() < NEAR_TIE, (rid, sel[i], want, gaps[i])
             mism += 1
     assert mism <= 2
+    # finite gaps were compared: the pool boundary wherever not every address
+    # is probed, the rerank boundary wherever the pool outgrows R (rare in the
+    # six-block case, whose lists hold 6 blocks over 64 addresses)
+    assert n_gaps[0] > 0 or cfg.n_probes >= cfg.A
+    assert n_gaps[1] > 0 or cfg_name == "tiny"
+
+
+# ------------------------------------------------ routing ties and gaps ----
+# Hand-built one-head cases with the identity rotation (cos = 1, sin = 0) and
+# one token per block, so every summary, code score, address score and rerank
+# score below is an exact small dyadic number and each decision can be
+# checked by hand.  Ties break toward the lowest index (the lowest address in
+# the walk, the lowest block in the rerank), as the routing rule states.
+def hand_route(orc, keys, query, cb, *, R=1, n_probes=1, L=1, cap=4):
+    """Index T blocks of one token (keys [T, d]) and route the last token
+    (query [d]).  cb is [P, K, d/P].  Returns (addr, sel, gaps)."""
+    keys = np.asarray(keys, np.float32)
+    T, d = keys.shape
+    P, K = cb.shape[0], cb.shape[1]
+    cos, sin = identity_table(T, d)
+    sh = shape(orc, B=1, T=T, Hq=1, Hkv=1, d=d, beta=1, P=P, K=K, cap=cap,
+               n_probes=n_probes, R=R, L=L)
+    cb4 = np.asarray(cb, np.float32).reshape(1, P, K, d // P)
+    idx = orc.build_index(sh, keys.reshape(1, T, 1, d), cos, sin, cb4)
+    q = np.zeros((1, T, 1, d), np.float32)
+    q[0, T - 1, 0] = query
+    sel, gaps = orc.route(sh, q, cos, sin, cb4, idx, np.array([T - 1]))
+    return idx["addr"].ravel().tolist(), sel[0].tolist(), gaps[0].tolist()
+
+
+# two components of two codes each: +x and +y of a 2-dim sub-vector
+AXES2 = np.array([[[1, 0], [0, 1]], [[1, 0], [0, 1]]], np.float32)
+
+
+def test_address_score_tie_goes_to_lower_address(orc):
+    """Blocks 0 and 1 sit at addresses 2 = (1, 0) and 1 = (0, 1); the query
+    (1, 0 | 1, 0) scores component codes (1, 0) and (1, 0), so
+    sigma = 2, 1, 1, 0 for addresses 0..3.  Address 0 holds no block; the
+    next two addresses tie at sigma 1 and the walk takes address 1 first:
+    with one probe and R = 1 the pool is its block 1, the selection [1].
+    Taking the tie toward the higher address would select block 0.  The
+    pool boundary (address 1 against address 2) has gap 0; the pool holds R
+    blocks, so no rerank decision is taken (+inf)."""
+    keys = [[0, 1, 1, 0],      # block 0 -> codes (1, 0) -> address 2
+            [1, 0, 0, 1],      # block 1 -> codes (0, 1) -> address 1
+            [0, 1, 0, 1]]      # block 2 (the query's own) -> address 3
+    addr, sel, gaps = hand_route(orc, keys, [1, 0, 1, 0], AXES2)
+    assert addr == [2, 1, 3]
+    assert sel == [1]
+    assert gaps[0] == 0.0 and gaps[1] == math.inf
+
+
+def test_address_score_clear_decision_and_its_gap(orc):
+    """The case above with the query (1, 0 | 0.75, 0.25): sigma = 1.75,
+    1.25, 0.75, 0.25.  Address 1 is now strictly ahead of address 2, the
+    selection is again [1], and the pool boundary gap is
+    (1.25 - 0.75) / 1.25 = 0.4, far above the near-tie bound."""
+    keys = [[0, 1, 1, 0], [1, 0, 0, 1], [0, 1, 0, 1]]
+    addr, sel, gaps = hand_route(orc, keys, [1, 0, 0.75, 0.25], AXES2)
+    assert addr == [2, 1, 3] and sel == [1]
+    assert gaps[0] == 0.4 and gaps[1] == math.inf
+    # the query (0, 1 | 1, 0) puts address 2 = (1, 0) first: sigma 2; then
+    # addresses 0 and 3 tie at 1 (both empty or ineligible) and address 1 is
+    # last.  Block 0 is taken at the first probe; boundary gap (2 - 1) / 2.
+    addr, sel, gaps = hand_route(orc, keys, [0, 1, 1, 0], AXES2)
+    assert sel == [0] and gaps[0] == 0.5
+
+
+# one component of two codes, +x and -x of the 4-dim key: every key with a
+# positive first coordinate (and every zero key: a tie, code 0) is address 0
+PLUS_MINUS_X = np.array([[[1, 0, 0, 0], [-1, 0, 0, 0]]], np.float32)
+
+
+def test_rerank_tie_on_zero_keys_goes_to_lower_blocks(orc):
+    """Zero keys give zero summaries, address 0 (both codes score 0; the tie
+    takes code 0) and a rerank score of exactly 0 for every block.  The
+    query block is 4 and L = 1, so blocks 0..3 are eligible and all four sit
+    in the one list probed.  R = 2 keeps the two lowest blocks, [0, 1]
+    (toward the highest would give [2, 3]); the rerank boundary gap is 0;
+    the pool boundary (address 0 at sigma 0.5 against address 1 at -0.5)
+    has gap 2."""
+    keys = np.zeros((5, 4), np.float32)
+    addr, sel, gaps = hand_route(orc, keys, [0.5, 1, 2, 3], PLUS_MINUS_X, R=2)
+    assert addr == [0] * 5
+    assert sel == [0, 1]
+    assert gaps == [2.0, 0.0]
+
+
+def test_rerank_duplicate_keys_and_clear_gap(orc):
+    """Blocks 1 and 3 carry the same key, the best rerank score (1.5) for
+    the query (1, 1, 1, 1): with R = 1 the tie keeps block 1 (gap 0).  With
+    R = 2 both are kept and the boundary against the next best (block 0,
+    score 0.5) has gap (1.5 - 0.5) / 1.5 = 2/3."""
+    keys = [[0.25, 0.25, 0, 0],     # rho 0.5
+            [0.5, 0.5, 0.25, 0.25],  # rho 1.5
+            [0.125, 0, 0, 0],        # rho 0.125
+            [0.5, 0.5, 0.25, 0.25],  # rho 1.5 (duplicate of block 1)
+            [1, 0, 0, 0]]            # the query's own block
+    addr, sel, gaps = hand_route(orc, keys, [1, 1, 1, 1], PLUS_MINUS_X, R=1)
+    assert addr == [0] * 5 and sel == [1] and gaps[1] == 0.0
+    addr, sel, gaps = hand_route(orc, keys, [1, 1, 1, 1], PLUS_MINUS_X, R=2)
+    assert sel == [1, 3] and gaps[1] == (1.5 - 0.5) / 1.5
+    # three slots: blocks 1, 3 and 0; the dropped block 2 (0.125) against
+    # block 0 (0.5): gap 0.75
+    addr, sel, gaps = hand_route(orc, keys, [1, 1, 1, 1], PLUS_MINUS_X, R=3)
+    assert sel == [0, 1, 3] and gaps[1] == 0.75
+
+
+def test_zero_query_walks_addresses_in_order(orc):
+    """A zero query scores every address 0: the walk visits addresses in
+    ascending order and every rerank score is 0.  Blocks 0..5 sit at
+    addresses 3, 1, 1, 2, 0, 3 (query block 6, L = 1).  With two probes and
+    R = 3 the walk takes address 0 (block 4), address 1 (blocks 1, 2): the
+    pool reaches 3 at the second address.  The rerank ties keep the lowest
+    three blocks of the pool, all of it: [1, 2, 4]."""
+    keys = [[0, 1, 0, 1],      # (1, 1) -> 3
+            [1, 0, 0, 1],      # (0, 1) -> 1
+            [1, 0, 0, 1],      # (0, 1) -> 1
+            [0, 1, 1, 0],      # (1, 0) -> 2
+            [1, 0, 1, 0],      # (0, 0) -> 0
+            [0, 1, 0, 1],      # (1, 1) -> 3
+            [1, 0, 1, 0]]      # the query's own block
+    addr, sel, gaps = hand_route(orc, keys, [0, 0, 0, 0], AXES2, R=3, n_probes=2)
+    assert addr == [3, 1, 1, 2, 0, 3, 0]
+    assert sel == [1, 2, 4]
+    assert gaps == [0.0, math.inf]
+    # R = 2: the pool is still blocks 4, 1, 2 (whole lists); the tie keeps 1, 2
+    addr, sel, gaps = hand_route(orc, keys, [0, 0, 0, 0], AXES2, R=2, n_probes=1)
+    assert sel == [1, 2] and gaps == [0.0, 0.0]
 
 
 @pytest.mark.parametrize("cfg", [configs.TINY,
