@@ -29,11 +29,15 @@
 //  4. The walk in rank order stops once >= n_probes addresses were probed
 //     and >= R blocks collected; equivalently the pool is every indexed
 //     eligible block whose address key is <= max(tau, key_R), key_R being
-//     the key of the R-th best indexed eligible block.  Lanes whose first
-//     n_probes lists hold < R eligible blocks need key_R: the wave scans the
-//     eligible blocks, keeping the R best block keys (R <= 2: one pass over
-//     values plus the batches they came from; larger R: one pass over values
-//     and a second that collects the blocks).
+//     the key of the address that holds the R-th eligible block in walk
+//     order.  Lanes whose first n_probes lists hold < R eligible blocks need
+//     key_R, which lies among the R best addresses that hold an eligible
+//     block.  The wave scans the workgroup's list of such addresses, kept
+//     in ascending address order, so that of two equal sums the lower
+//     address is met first and kept (R <= 2: one pass over values plus the
+//     batches they came from; larger R: one pass over values and a second
+//     that collects the addresses).  The scan is bounded by the number of
+//     addresses, whatever the sequence length.
 //  5. Rerank: rho = fp32 fma chain <q_rot, kbar_n> in dimension order; the
 //     R best by (rho desc, block asc) are kept and written ascending.
 //
@@ -48,8 +52,10 @@ namespace {
 
 typedef unsigned long long u64;
 
+// Order-preserving map of a float to an unsigned integer; -0 is taken as +0,
+// as the float comparison takes it.
 __device__ __forceinline__ uint32_t ordered(float f) {
-    const uint32_t u = __float_as_uint(f);
+    const uint32_t u = __float_as_uint(f + 0.0f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
@@ -69,13 +75,18 @@ __device__ __forceinline__ void insert(u64 (&lst)[M], u64 k) {
     }
 }
 
-// Blocks the extension scan reads past the last eligible one (its row
-// offsets are loaded two batches ahead).
+// Entries the extension scan reads past the end of the address list (its
+// row offsets are loaded two batches ahead).
 constexpr int SCAN_U = 8, SCAN_PAD = 2 * SCAN_U;
 
-// Float offset of the per-wave score areas (after the lists, 16-byte aligned).
+// Addresses the extension's list can hold: those with an indexed block.
+__host__ __device__ constexpr int route_list_max(int NB, int A) { return NB < A ? NB : A; }
+
+// Workgroup LDS, in 4-byte words: the address list (int2 score-row offsets,
+// list_max + SCAN_PAD entries), its length, the list offsets [A + 1] and the
+// list entries [NB]; then the per-wave score areas, 16-byte aligned.
 __host__ __device__ constexpr int route_sc_off(int NB, int A) {
-    return (3 * NB + 2 * SCAN_PAD + A + 1 + 3) & ~3;
+    return (2 * (route_list_max(NB, A) + SCAN_PAD) + 1 + A + 1 + NB + 3) & ~3;
 }
 
 // Floats per score row: 64 lanes plus 4 of padding, so the 16 rows one
@@ -112,8 +123,10 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
     extern __shared__ float lds[];
     const int K = s.K, PK = P * K, A = s.A, NB = s.NB;
     const int nw = blockDim.x / WAVE;
-    int2 *meta_s = reinterpret_cast<int2 *>(lds);                // [NB + SCAN_PAD]: score-row offsets
-    int *off_s = reinterpret_cast<int *>(meta_s + NB + SCAN_PAD);   // [A+1]
+    const int LMAX = route_list_max(NB, A);
+    int2 *alist = reinterpret_cast<int2 *>(lds);                 // [LMAX + SCAN_PAD]: score-row offsets
+    int *nal_s = reinterpret_cast<int *>(alist + LMAX + SCAN_PAD);   // list length
+    int *off_s = nal_s + 1;                                      // [A+1]
     int *ent_s = off_s + A + 1;                                  // [NB]
     float *sc_all = reinterpret_cast<float *>(lds) + route_sc_off(NB, A);   // [nw][...][64]
     const int lane = lane_id(), wave = uniform(threadIdx.x / WAVE);
@@ -143,39 +156,28 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
     const int tq = min(t, s.T - 1);        // clamped: the loads below stay in bounds
     const size_t qbase = (((size_t)b * s.T + tq) * s.Hq + h) * D;
 
-    // List offsets, list entries and block addresses of the (batch,
-    // kv-head) are staged in LDS.  Every thread issues its loads of a round
-    // (indexes clamped, so none is predicated) before storing any; the
-    // addresses go to the row-offset table and are converted below.  The
-    // first round's loads are issued before the wave's own loads, so its
-    // stores wait for them only.
+    // List offsets and list entries of the (batch, kv-head) are staged in
+    // LDS.  Every thread issues its loads of a round (indexes clamped, so
+    // none is predicated) before storing any.  The first round's loads are
+    // issued before the wave's own loads, so its stores wait for them only.
     const int32_t *off_g = offsets + ug * (A + 1);
     const int32_t *ent_g = entries + ug * NB;
     const int32_t *ad_g = addr + ug * NB;
-    int *meta_i = reinterpret_cast<int *>(meta_s);
     const int bd = blockDim.x, tid = threadIdx.x;
-    int vo[STAGE_OFF], ve[STAGE_BLK], va[STAGE_BLK];
+    int vo[STAGE_OFF], ve[STAGE_BLK];
     auto stage_load = [&](int r0) {
 #pragma unroll
         for (int u = 0; u < STAGE_OFF; ++u) vo[u] = off_g[min(r0 + u * bd + tid, A)];
 #pragma unroll
-        for (int u = 0; u < STAGE_BLK; ++u) {
-            const int i = min(r0 / 2 + u * bd + tid, NB - 1);
-            ve[u] = ent_g[i];
-            va[u] = ad_g[i];
-        }
+        for (int u = 0; u < STAGE_BLK; ++u) ve[u] = ent_g[min(r0 / 2 + u * bd + tid, NB - 1)];
     };
     // (stores use the same clamped indexes: threads past the end rewrite the
-    // last element with its own value; addresses past nblk are never read)
+    // last element with its own value)
     auto stage_store = [&](int r0) {
 #pragma unroll
         for (int u = 0; u < STAGE_OFF; ++u) off_s[min(r0 + u * bd + tid, A)] = vo[u];
 #pragma unroll
-        for (int u = 0; u < STAGE_BLK; ++u) {
-            const int i = min(r0 / 2 + u * bd + tid, NB - 1);
-            ent_s[i] = ve[u];
-            meta_i[2 * i] = va[u];
-        }
+        for (int u = 0; u < STAGE_BLK; ++u) ent_s[min(r0 / 2 + u * bd + tid, NB - 1)] = ve[u];
     };
     if (any_search) stage_load(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -254,21 +256,53 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
         }
     }
     __syncthreads();
+    // Byte offsets of the score-table rows of an address's component codes
+    // (relative to the lane's column), and the address back from them.
+    auto row_offsets = [&](int a) {
+        const int c0 = P == 1 ? a : a / K, c1 = P == 1 ? 0 : a - c0 * K;
+        return make_int2(c0 * SROW * 4, P == 1 ? dummy : (K + c1) * SROW * 4);
+    };
+    auto addr_of = [&](int2 m) {
+        const int c0 = m.x / (SROW * 4);
+        return P == 1 ? c0 : c0 * K + (m.y / (SROW * 4) - K);
+    };
+    // the first wave's last eligible block (later waves have later ones)
+    const int last0 = tw0 / s.beta - s.L;
     if (any_search) {
-        for (int n = threadIdx.x; n < nblk; n += blockDim.x) {
-            const int a = meta_s[n].x;
-            // kept blocks are the first `cap` of the address in source order,
-            // so n is indexed iff it is not after the list's last entry.
-            // Byte offsets of the score-table rows of the block's component
-            // codes; a block that is not indexed points at the -inf row.
-            const int c0 = P == 1 ? a : a / K, c1 = P == 1 ? 0 : a - c0 * K;
-            const bool idx = n <= ent_s[off_s[a + 1] - 1];
-            const int o0 = c0 * SROW * 4, o1 = P == 1 ? dummy : (K + c1) * SROW * 4;
-            meta_s[n] = idx ? make_int2(o0, o1) : make_int2(dummy, dummy);
+        // The extension's address list: every address whose first (lowest)
+        // indexed block is eligible for the workgroup's first wave, in
+        // ascending address order.  Thread t owns addresses
+        // [t * per, (t + 1) * per); a workgroup scan of the counts places
+        // them.  The scan's read-ahead past the end lands on the -inf row.
+        const int per = (A + bd - 1) / bd;
+        const int a_lo = min(tid * per, A), a_hi = min(a_lo + per, A);
+        int c = 0;
+        for (int a = a_lo; a < a_hi; ++a) {
+            const int e0 = off_s[a];
+            c += (e0 < off_s[a + 1] && ent_s[e0] <= last0) ? 1 : 0;
         }
-        // the scan's read-ahead past the eligible blocks lands on the -inf row
-        for (int n = nblk + (int)threadIdx.x; n < nblk + SCAN_PAD; n += blockDim.x)
-            meta_s[n] = make_int2(dummy, dummy);
+        int x = c;
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            x += lane >= o ? y : 0;
+        }
+        // the score areas are not in use yet: wave totals go there
+        int *wsum = reinterpret_cast<int *>(sc_all);
+        if (lane == WAVE - 1) wsum[wave] = x;
+        __syncthreads();
+        int pos = x - c, tot = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int v = wsum[w];
+            pos += w < wave ? v : 0;
+            tot += v;
+        }
+        for (int a = a_lo; a < a_hi; ++a) {
+            const int e0 = off_s[a];
+            if (e0 < off_s[a + 1] && ent_s[e0] <= last0) alist[pos++] = row_offsets(a);
+        }
+        for (int i = tid; i < SCAN_PAD; i += bd) alist[tot + i] = make_int2(dummy, dummy);
+        if (tid == 0) *nal_s = tot;
     }
     __syncthreads();
 
@@ -645,22 +679,18 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
     int cnt = 0;
     if (live) walk_part1([&](int n) { add(n); ++cnt; });
 
-    sc_s[PK * SROW + lane] = -INFINITY;   // the row unindexed blocks point at
+    sc_s[PK * SROW + lane] = -INFINITY;   // the row past-the-end list entries point at
 
-    // ---- pool part 2: extension to R blocks, for lanes that need it.  The
-    // R best eligible indexed blocks by (sigma desc, block asc), visited in
-    // source order; a new block enters only if its sigma beats the R-th best.
-    // Blocks of different addresses with bitwise equal sigma are ordered by
-    // block rather than address (an exact score tie at the pool boundary).
-    // RM - R sentinel slots never move.
+    // ---- pool part 2: the extension, for lanes whose part 1 holds fewer
+    // than R blocks.  The R best addresses holding an eligible block, by
+    // (sigma desc, address asc), as 64-bit keys, best first: a scan of the
+    // workgroup's address list, then the few addresses whose first block
+    // became eligible after the workgroup's first wave (inserted with their
+    // full keys).  RM - R sentinel value slots never move.
     const bool need = live && cnt < R;
-    float bs[RM];
-    int bn[RM];
+    u64 top[RM];
 #pragma unroll
-    for (int x = 0; x < RM; ++x) { bs[x] = x < RM - R ? INFINITY : -INFINITY; bn[x] = -1; }
-    // more than two slots: the R-th best sigma and the R-th best block
-    float vR = -INFINITY;
-    int nR = -1;
+    for (int x = 0; x < RM; ++x) top[x] = 0ull;
     const char *scl = reinterpret_cast<const char *>(sc_s + lane);
     auto sigma = [&](int2 m) {
         const float a0 = *reinterpret_cast<const float *>(scl + m.x);
@@ -668,24 +698,24 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
         const float a1 = *reinterpret_cast<const float *>(scl + m.y);
         return a0 + a1;
     };
+    auto addr_key = [&](float sg, int a) { return key_of(sg, (uint32_t)(0x7FFFFFFF - a)); };
+    auto key_addr = [](u64 k) { return 0x7FFFFFFF - (int)(k & 0xFFFFFFFFu); };
     if (__ballot(need) != 0ull) {
-        // Two slots: the list is sorted and a new block's id exceeds every
-        // resident's, so only the new block is compared (strictly: a
-        // resident of equal sigma has the lower id).  More slots: the scan
-        // keeps the values only (slot x takes the median of old slots x - 1,
-        // x and the new sigma, slot 0 the larger of the two), and a second
-        // pass recovers the blocks.  Lanes that need no extension update
-        // lists they never read.
-        // more slots, first pass: the values only
+        const int nal = *nal_s;
+        float bs[RM];
+#pragma unroll
+        for (int x = 0; x < RM; ++x) bs[x] = x < RM - R ? INFINITY : -INFINITY;
+        // more slots, first pass: the values only (slot x takes the median of
+        // old slots x - 1, x and the new sigma, slot 0 the larger of the two)
         auto visit = [&](float sg) {
 #pragma unroll
             for (int x = RM - 1; x > 0; --x) bs[x] = __builtin_amdgcn_fmed3f(bs[x - 1], bs[x], sg);
             bs[0] = __builtin_amdgcn_fmed3f(bs[0], sg, INFINITY);
         };
-        // Software pipeline over batches of U blocks: the row offsets are
-        // loaded two batches ahead and the score gathers one batch ahead,
-        // so the work on a batch overlaps the next batch's LDS reads.  The
-        // read-ahead stays inside the padded offsets (-inf rows).
+        // Software pipeline over batches of U list entries: the row offsets
+        // are loaded two batches ahead and the score gathers one batch
+        // ahead, so the work on a batch overlaps the next batch's LDS reads.
+        // The read-ahead stays inside the padded list (-inf rows).
         constexpr int U = SCAN_U;
         auto gather = [&](const int2 (&m)[U], float (&a)[U], float (&c)[U]) {
 #pragma unroll
@@ -696,9 +726,9 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
         };
         // Two slots: the scan keeps the two values only (slot 1 takes the
         // median of old slot 0, old slot 1 and the new sigma; slot 0 the
-        // larger), plus the batch each slot's block came from: a batch that
-        // raises slot 0 gives it its first block of that sigma; slot 1 then
-        // holds the batch's runner-up or the old slot 0.  The block ids are
+        // larger), plus the batch each slot's address came from: a batch that
+        // raises slot 0 gives it its first address of that sigma; slot 1 then
+        // holds the batch's runner-up or the old slot 0.  The addresses are
         // recovered afterwards from those two batches.
         float v0 = bs[0], v1 = bs[RM - 1];
         int bb0 = -1, bb1 = -1;
@@ -720,23 +750,23 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
             v0 = n0;
             v1 = n1;
         };
-        // one pass over the blocks 0..last in batches of U: consume(sg, n0)
-        // gets the sigmas of blocks n0 .. n0 + U - 1 (-inf past last)
+        // one pass over the list in batches of U: consume(sg, i0) gets the
+        // sigmas of entries i0 .. i0 + U - 1 (-inf past the end)
         auto scan = [&](auto &&consume) {
             int n = 0;
-            if (U <= last + 1) {
+            if (U <= nal) {
                 int2 m[U];
                 float a0[U], c0[U], a1[U], c1[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) m[u] = meta_s[u];
+                for (int u = 0; u < U; ++u) m[u] = alist[u];
                 gather(m, a0, c0);
 #pragma unroll
-                for (int u = 0; u < U; ++u) m[u] = meta_s[U + u];
+                for (int u = 0; u < U; ++u) m[u] = alist[U + u];
                 // two batches per trip, so the buffers alternate without copies
                 while (true) {
                     gather(m, a1, c1);                              // batch n + U
 #pragma unroll
-                    for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
+                    for (int u = 0; u < U; ++u) m[u] = alist[n + 2 * U + u];
                     __builtin_amdgcn_sched_barrier(0);
                     {
                         float sg[U];
@@ -746,10 +776,10 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     n += U;
-                    if (n + U > last + 1) break;
+                    if (n + U > nal) break;
                     gather(m, a0, c0);                              // batch n + U
 #pragma unroll
-                    for (int u = 0; u < U; ++u) m[u] = meta_s[n + 2 * U + u];
+                    for (int u = 0; u < U; ++u) m[u] = alist[n + 2 * U + u];
                     __builtin_amdgcn_sched_barrier(0);
                     {
                         float sg[U];
@@ -759,104 +789,124 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     n += U;
-                    if (n + U > last + 1) break;
+                    if (n + U > nal) break;
                 }
             }
             // the partial last batch (its padded read-ahead rows are -inf)
-            if (n <= last) {
+            if (n < nal) {
                 float sg[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const float v = sigma(meta_s[n + u]);
-                    sg[u] = n + u <= last ? v : -INFINITY;
+                    const float v = sigma(alist[n + u]);
+                    sg[u] = n + u < nal ? v : -INFINITY;
                 }
                 consume(sg, n);
             }
         };
         if constexpr (RM == 2) {
-            scan([&](const float (&sg)[U], int n0) { batch_vals(sg, n0 / U); });
-            // the first block of a batch whose sigma equals val, other than excl
+            scan([&](const float (&sg)[U], int i0) { batch_vals(sg, i0 / U); });
+            // the first entry of a batch whose sigma equals val, other than excl
             auto find = [&](int batch, float val, int excl) {
                 int res = -1;
                 if (batch >= 0) {
 #pragma unroll
                     for (int u = U - 1; u >= 0; --u) {
-                        const int nn = batch * U + u;
-                        const bool hit = nn <= last && nn != excl && sigma(meta_s[nn]) == val;
-                        res = hit ? nn : res;
+                        const int i = batch * U + u;
+                        const bool hit = i < nal && i != excl && sigma(alist[i]) == val;
+                        res = hit ? i : res;
                     }
                 }
                 return res;
             };
-            bn[0] = RM - R == 0 && v0 > -INFINITY ? find(bb0, v0, -1) : -1;
-            bn[1] = v1 > -INFINITY ? find(bb1, v1, bn[0]) : -1;
-            bs[0] = v0;
-            bs[1] = v1;
+            const int i0 = RM - R == 0 && v0 > -INFINITY ? find(bb0, v0, -1) : -1;
+            const int i1 = v1 > -INFINITY ? find(bb1, v1, i0) : -1;
+            const u64 k0 = i0 >= 0 ? addr_key(v0, addr_of(alist[i0])) : 0ull;
+            const u64 k1 = i1 >= 0 ? addr_key(v1, addr_of(alist[i1])) : 0ull;
+            top[0] = RM - R == 0 ? k0 : k1;
+            top[1] = RM - R == 0 ? k1 : 0ull;
         } else {
-            scan([&](const float (&sg)[U], int n0) {
+            scan([&](const float (&sg)[U], int) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) visit(sg[u]);
             });
-            // The R best are the blocks above the R-th value plus the first
-            // blocks (source order) equal to it, as many as slots hold that
-            // value; none if that value is -inf (fewer than R indexed
-            // blocks).  The second pass shifts them into bn (latest first)
-            // and keeps the last equal one: the R-th best block.  (Lanes
-            // that need no extension fill lists they never read.)
-            vR = bs[RM - 1];
+            // The R best are the entries above the R-th value plus the first
+            // entries (list order) equal to it, as many as slots hold that
+            // value; none if that value is -inf (fewer than R addresses).
+            // The second pass shifts their positions into ti.
+            const float vR = bs[RM - 1];
             int eq_left = 0;
 #pragma unroll
             for (int x = 0; x < RM; ++x) eq_left += (x >= RM - R && bs[x] == vR) ? 1 : 0;
             if (vR == -INFINITY) eq_left = 0;
-            scan([&](const float (&sg)[U], int n0) {
+            int ti[RM];
+#pragma unroll
+            for (int x = 0; x < RM; ++x) ti[x] = -1;
+            scan([&](const float (&sg)[U], int i0) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const bool eq = (sg[u] == vR) & (eq_left > 0);
                     const bool take = (sg[u] > vR) | eq;
                     eq_left -= eq ? 1 : 0;
-                    nR = eq ? n0 + u : nR;
 #pragma unroll
-                    for (int x = RM - 1; x > 0; --x) bn[x] = take ? bn[x - 1] : bn[x];
-                    bn[0] = take ? n0 + u : bn[0];
+                    for (int x = RM - 1; x > 0; --x) ti[x] = take ? ti[x - 1] : ti[x];
+                    ti[0] = take ? i0 + u : ti[0];
                 }
             });
+#pragma unroll
+            for (int x = 0; x < RM; ++x) {
+                if (ti[x] >= 0) {
+                    const int2 m = alist[ti[x]];
+                    insert(top, addr_key(sigma(m), addr_of(m)));
+                }
+            }
+        }
+        // addresses whose first block is eligible for this wave but not for
+        // the workgroup's first one (at most the blocks between their last
+        // eligible blocks): their full keys go into the list
+        for (int n = max(0, last0 + 1); n <= last; ++n) {
+            const int a = min(max(ad_g[n], 0), A - 1);    // (clamped: reads stay in bounds)
+            if (ent_s[min(off_s[a], NB - 1)] == n) {
+                const int2 m = row_offsets(a);
+                insert(top, addr_key(sigma(m), a));
+            }
         }
     }
-    // address of an indexed block, from its score-row offsets
-    auto addr_of = [&](int nn) {
-        const int2 m = meta_s[nn];
-        const int c0 = m.x / (SROW * 4);
-        return P == 1 ? c0 : c0 * K + (m.y / (SROW * 4) - K);
-    };
+    // The addresses up to the one holding the R-th eligible block in walk
+    // order (their eligible counts, in key order, reach R there) join the
+    // pool; all of the R if their blocks do not reach R (then every address
+    // holding an eligible block is among them: the walk probes everything).
+    int nadd = 0;
+    if (need) {
+        int cum = 0;
+#pragma unroll
+        for (int x = 0; x < RM; ++x) {
+            if (x < R && top[x] != 0ull && cum < R) {
+                const int a = key_addr(top[x]);
+                const int e1 = off_s[a + 1];
+                for (int e = off_s[a]; e < e1 && ent_s[e] <= last; ++e) ++cum;
+                nadd = x + 1;
+            }
+        }
+    }
     // does (sigma, address) rank after the n_probes-th address?
     auto after_tau = [&](float sg, int a) {
         return (sg < tau_v) | ((sg == tau_v) & (a > tau_a));
     };
-    // the extension's pool members: the R best blocks that rank after tau
-    // (the others are in part 1), then the blocks of the R-th block's
-    // address after it (they tie with it)
+    // the extension's pool members: the eligible blocks of those addresses
+    // that rank after tau (the others are in part 1)
     auto walk_ext = [&](auto &&fn) {
         if (!need) return;
 #pragma unroll
         for (int x = 0; x < RM; ++x) {
-            if constexpr (RM == 2) {
-                if (x < RM - R || bn[x] < 0) continue;
-                if (after_tau(bs[x], addr_of(bn[x]))) fn(bn[x]);
-            } else {
-                if (bn[x] < 0) continue;
-                if (after_tau(sigma(meta_s[bn[x]]), addr_of(bn[x]))) fn(bn[x]);
-            }
-        }
-        const int nR_ = RM == 2 ? bn[RM - 1] : nR;
-        const float vR_ = RM == 2 ? bs[RM - 1] : vR;
-        if (nR_ >= 0) {
-            const int aR = addr_of(nR_);
-            if (after_tau(vR_, aR)) {
-                const int e1 = off_s[aR + 1];
-                for (int e = off_s[aR]; e < e1; ++e) {
-                    const int nn = ent_s[e];
-                    if (nn > last) break;
-                    if (nn > nR_) fn(nn);
+            if (x < nadd) {
+                const int a = key_addr(top[x]);
+                if (after_tau(sigma(row_offsets(a)), a)) {
+                    const int e1 = off_s[a + 1];
+                    for (int e = off_s[a]; e < e1; ++e) {
+                        const int nn = ent_s[e];
+                        if (nn > last) break;
+                        fn(nn);
+                    }
                 }
             }
         }

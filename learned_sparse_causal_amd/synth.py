@@ -183,3 +183,21 @@ def concentrated_keys(cfg: Config, seed, model_seed=40, n_topics=8, shared=1.0, 
         blockwise = mu[g][None, None, :] + nu[g][pick[:, :, g]]          # [B, NB, d]
         k[:, :, g, :] += np.repeat(blockwise, cfg.beta, axis=1)
     return _cast(k, cfg.dtype), cb
+
+
+def tied_inputs(cfg: Config, zero_key_every=5, zero_query_every=7):
+    """The `qkv` draws rearranged so that routing meets exact score ties:
+    every `zero_key_every`-th block of keys (blocks 1, 1 + every, ...) is
+    zeroed in every kv-head, every `zero_query_every`-th query token is
+    zeroed in every head, and in every component code 1 repeats code 0 and
+    code K-1 repeats code 2 (K >= 4).  Layout only: rows are zeroed or
+    copied, nothing is computed.  Returns dict(q, k, v, codebooks)."""
+    inp = qkv(cfg)
+    q, k, cb = inp["q"].copy(), inp["k"].copy(), inp["codebooks"].copy()
+    for n in range(1, cfg.NB, zero_key_every):
+        k[:, n * cfg.beta:(n + 1) * cfg.beta] = 0.0
+    q[:, ::zero_query_every] = 0.0
+    if cfg.K >= 4:
+        cb[:, :, 1] = cb[:, :, 0]
+        cb[:, :, cfg.K - 1] = cb[:, :, 2]
+    return dict(q=q, k=k, v=inp["v"], codebooks=np.ascontiguousarray(cb))

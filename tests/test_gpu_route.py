@@ -137,3 +137,34 @@ def test_route_deterministic():
     for k in a[0]:
         assert np.array_equal(a[0][k], b[0][k]), k
     assert np.array_equal(a[1], b[1])
+
+
+TIE_CFGS = [configs.SMALL.with_(name="ties_bf16_T4096"),
+            configs.sweep(8192).with_(name="ties_sweep_T8192"),
+            configs.SMALL.with_(name="ties_probes1_R1", n_probes=1, R=1, Hq=2, Hkv=2),
+            configs.SMALL.with_(name="ties_d128_f32_R8", d=128, beta=128, T=8192, Hq=2, Hkv=1,
+                                dtype="f32", n_probes=8, R=8),
+            configs.SMALL.with_(name="ties_P1_K64_R3", P=1, K=64, Hq=4, Hkv=2, R=3)]
+
+
+@pytest.mark.parametrize("cfg", TIE_CFGS, ids=lambda c: c.name)
+def test_route_exact_ties(orc, cfg):
+    """Exact score ties at every kind of decision, which the lowest-index
+    rule decides: zeroed key blocks (summary 0, every code score 0: code 0,
+    rerank score 0 for every query), zeroed query tokens (every address
+    score and rerank score 0: addresses walked in ascending order, lowest
+    blocks kept) and duplicated code rows (equal component scores).  The GPU
+    must take every such decision as the oracle does: no route is excused."""
+    say("[route] %s" % cfg.name)
+    inp = synth.tied_inputs(cfg)
+    g_idx, g_sel = run_gpu(cfg, dev(inp["q"], cfg.dtype), dev(inp["k"], cfg.dtype),
+                           inp["codebooks"])
+    o_idx, o_sel, gaps = run_oracle(orc, cfg, inp["q"], inp["k"], inp["codebooks"])
+    compare_index(cfg, g_idx, o_idx, excuse=False)
+    check_sel_invariants(cfg, g_sel, g_idx)
+    tied = int((gaps.min(-1) == 0.0).sum())
+    assert tied > 0, "the inputs produced no exact tie at a decision"
+    diff = np.nonzero((g_sel.reshape(-1, cfg.R) != o_sel).any(-1))[0]
+    assert len(diff) == 0, "%d routes differ (first %s: gpu %s oracle %s gaps %s)" % (
+        len(diff), diff[:1], g_sel.reshape(-1, cfg.R)[diff[:1]], o_sel[diff[:1]], gaps[diff[:1]])
+    say("  %d routes decided on an exact tie, all equal to the oracle" % tied)
