@@ -54,7 +54,9 @@ typedef enum {
                                  size, or n_q_heads*head_dim != width (mixer) */
     MONO_ERR_UNSUPPORTED = 3, /* consistent but outside the supported shapes above */
     MONO_ERR_WORKSPACE = 4,   /* ws_bytes smaller than mono_workspace_bytes() */
-    MONO_ERR_HIP = 5          /* a HIP launch failed */
+    MONO_ERR_HIP = 5,         /* a HIP launch failed */
+    MONO_ERR_SCRATCH = 6      /* mono_routed_attention_noalloc: the call needs more than
+                                 MONO_NOALLOC_SCRATCH_BYTES of scratch */
 } mono_status;
 
 typedef enum { MONO_F32 = 0, MONO_BF16 = 1 } mono_dtype;
@@ -196,6 +198,28 @@ mono_status mono_routed_attention(const mono_config *cfg, const void *q, const v
                                   const float *codebooks, const mono_index *idx, int32_t *sel,
                                   void *out, void *ws, size_t ws_bytes, void *const *stage_events,
                                   void *stream);
+
+/* Bytes of the library's static scratch area (per GPU) that
+ * mono_routed_attention_noalloc uses in place of a workspace: 128 MiB. */
+#define MONO_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* mono_routed_attention without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments (minus ws and
+ * ws_bytes), same results, same kernels.  The scratch it needs lives in a
+ * static device array of MONO_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds until the process ends; the call allocates and
+ * frees nothing.  Configurations whose MONO_WS_ATTENTION workspace exceeds
+ * that size return MONO_ERR_SCRATCH with nothing enqueued.  `stream` must
+ * belong to the current device.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller.  The array keeps the last call's
+ * contents; nothing in the step depends on its contents on entry. */
+mono_status mono_routed_attention_noalloc(const mono_config *cfg, const void *q, const void *k,
+                                          const void *v, const float *rope_cos,
+                                          const float *rope_sin, const float *codebooks,
+                                          const mono_index *idx, int32_t *sel, void *out,
+                                          void *const *stage_events, void *stream);
 
 /* Dense causal attention, the baseline the routed path is measured against
  * (news page, section "The 99.35 Percent Result Does Not Establish Language

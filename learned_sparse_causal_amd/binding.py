@@ -17,7 +17,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "mono.h")
 MONO_F32, MONO_BF16 = 0, 1
 WS_BUILD, WS_ROUTE, WS_ATTENTION, WS_MIXER, WS_DENSE, WS_CALIBRATE = 0, 1, 2, 3, 4, 5
 STATUS = {0: "MONO_OK", 1: "MONO_ERR_NULL", 2: "MONO_ERR_SHAPE", 3: "MONO_ERR_UNSUPPORTED",
-          4: "MONO_ERR_WORKSPACE", 5: "MONO_ERR_HIP"}
+          4: "MONO_ERR_WORKSPACE", 5: "MONO_ERR_HIP", 6: "MONO_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 128 << 20       # MONO_NOALLOC_SCRATCH_BYTES
 
 
 class MonoError(RuntimeError):
@@ -63,6 +64,7 @@ def load_library(path=LIB_PATH):
     lib.mono_selected_attention.argtypes = [cfgp, P, P, P, P, P, P, P, P, S, P]
     lib.mono_dense_attention.argtypes = [cfgp, P, P, P, P, P, P, P, S, P]
     lib.mono_routed_attention.argtypes = [cfgp, P, P, P, P, P, P, idxp, P, P, P, S, P, P]
+    lib.mono_routed_attention_noalloc.argtypes = [cfgp, P, P, P, P, P, P, idxp, P, P, P, P]
     lib.mono_calibrate_codebooks.argtypes = [cfgp, P, P, ctypes.c_int32, P, S, P]
     lib.mono_decode_index.argtypes = [cfgp, P, P, P, P, idxp, ctypes.c_int32, ctypes.c_int32, P]
     lib.mono_decode_step.argtypes = [cfgp, P, P, P, P, P, P, idxp, ctypes.c_int32, P, P, P]
@@ -71,7 +73,8 @@ def load_library(path=LIB_PATH):
     lib.mono_status_string.argtypes = [I]
     lib.mono_status_string.restype = ctypes.c_char_p
     for f in ("mono_rope_table", "mono_build_index", "mono_route", "mono_selected_attention",
-              "mono_dense_attention", "mono_routed_attention", "mono_calibrate_codebooks",
+              "mono_dense_attention", "mono_routed_attention", "mono_routed_attention_noalloc",
+              "mono_calibrate_codebooks",
               "mono_decode_index",
               "mono_decode_step",
               "mono_mixer_forward", "mono_mixer_layout"):
@@ -271,6 +274,38 @@ def routed_attention(cfg, q, k, v, rope_cos, rope_sin, codebooks, index=None, se
         _need(sel, (cfg.B, cfg.Hq, cfg.T, cfg.R), torch.int32, "sel"),
         _need(out, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "out"),
         ws.data_ptr() if ws is not None else None, nws, ev, _stream()))
+    return idx, sel, out
+
+
+def routed_attention_noalloc(cfg, q, k, v, rope_cos, rope_sin, codebooks, index=None, sel=None,
+                             out=None, stage_events=None):
+    """mono_routed_attention_noalloc: the whole step with the library's static
+    scratch in place of a workspace; returns (index, sel, out).  Outputs not
+    passed in are allocated here, by torch, before the call."""
+    torch = _torch()
+    c = make_config(cfg)
+    dt = _act_dtype(cfg)
+    idx = index if index is not None else empty_index(cfg)
+    st = _index_struct(cfg, idx)
+    if sel is None:
+        sel = torch.empty((cfg.B, cfg.Hq, cfg.T, cfg.R), dtype=torch.int32, device="cuda")
+    if out is None:
+        out = torch.empty((cfg.B, cfg.T, cfg.Hq, cfg.d), dtype=dt, device="cuda")
+    ev = None
+    if stage_events is not None:
+        ev = (ctypes.c_void_p * 4)(*_event_handles(stage_events))
+    _check(load_library().mono_routed_attention_noalloc(
+        ctypes.byref(c),
+        _need(q, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "q"),
+        _need(k, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "k"),
+        _need(v, (cfg.B, cfg.T, cfg.Hkv, cfg.d), dt, "v"),
+        _need(rope_cos, (cfg.T, cfg.d // 2), torch.float32, "rope_cos"),
+        _need(rope_sin, (cfg.T, cfg.d // 2), torch.float32, "rope_sin"),
+        _need(codebooks, (cfg.Hkv, cfg.P, cfg.K, cfg.d // cfg.P), torch.float32, "codebooks"),
+        ctypes.byref(st),
+        _need(sel, (cfg.B, cfg.Hq, cfg.T, cfg.R), torch.int32, "sel"),
+        _need(out, (cfg.B, cfg.T, cfg.Hq, cfg.d), dt, "out"),
+        ev, _stream()))
     return idx, sel, out
 
 

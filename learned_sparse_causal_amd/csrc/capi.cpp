@@ -53,6 +53,34 @@ hipError_t launch_gemm_qkv(int bf16, int M, int N, int Kd, const void *A, const 
                            void *k, void *v, int nq, int nk, hipStream_t st);
 
 namespace {
+// Static scratch of mono_routed_attention_noalloc.  Host code never passes
+// this name to a kernel (on the host it is a stand-in, not a device
+// address): the device address comes from hipGetSymbolAddress, once per
+// device, and is kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[MONO_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (set up on the
+// first call on that device, with that device current).
+hipError_t scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
 std::mutex g_cache_mutex;
 std::map<std::pair<const void *, int>, size_t> g_lds_set;                  // (kernel, device)
 std::map<std::tuple<const void *, int, int, size_t>, long> g_resident;    // (.., threads, lds)
@@ -298,6 +326,25 @@ mono_status mono_routed_attention(const mono_config *cfg, const void *q, const v
     return MONO_OK;
 }
 
+mono_status mono_routed_attention_noalloc(const mono_config *cfg, const void *q, const void *k,
+                                          const void *v, const float *rope_cos,
+                                          const float *rope_sin, const float *codebooks,
+                                          const mono_index *idx, int32_t *sel, void *out,
+                                          void *const *stage_events, void *stream) {
+    Shape s;
+    const mono_status st = make_shape(cfg, false, s);
+    if (st != MONO_OK) return st;
+    if (!q || !k || !v || !rope_cos || !rope_sin || !codebooks || !index_ok(idx) || !sel || !out)
+        return MONO_ERR_NULL;
+    size_t off[14];
+    const size_t need = attention_ws_layout(s, off);
+    if (need > MONO_NOALLOC_SCRATCH_BYTES) return MONO_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess) return MONO_ERR_HIP;
+    return mono_routed_attention(cfg, q, k, v, rope_cos, rope_sin, codebooks, idx, sel, out, ws,
+                                 need, stage_events, stream);
+}
+
 mono_status mono_dense_attention(const mono_config *cfg, const void *q, const void *k,
                                  const void *v, const float *rope_cos, const float *rope_sin,
                                  void *out, void *ws, size_t ws_bytes, void *stream) {
@@ -425,6 +472,9 @@ const char *mono_status_string(mono_status status) {
         case MONO_ERR_UNSUPPORTED: return "shape or dtype outside the supported set";
         case MONO_ERR_WORKSPACE: return "workspace too small";
         case MONO_ERR_HIP: return "a HIP launch failed";
+        case MONO_ERR_SCRATCH:
+            return "the call needs more scratch than the static area holds "
+                   "(MONO_NOALLOC_SCRATCH_BYTES); use the workspace entry point";
     }
     return "unknown status";
 }

@@ -149,3 +149,23 @@ def test_decode_argument_errors(lib):
                                 -1, one, one, None) == 2
     assert lib.mono_decode_step(ctypes.byref(c), one, one, one, one, one, one, ctypes.byref(idx),
                                 0, None, one, None) == 1
+
+
+def test_noalloc_argument_errors(lib):
+    """mono_routed_attention_noalloc validates on the host before touching the
+    device: NULL pointers, bad shapes, and a workload whose attention
+    workspace exceeds the static scratch (MONO_ERR_SCRATCH)."""
+    small = binding.make_config(configs.SMALL)
+    big = binding.make_config(configs.SWEEP_32K)
+    idx = binding.MonoIndex(*([1] * 6))
+    p = ctypes.c_void_p(1)
+    fn = lib.mono_routed_attention_noalloc
+    assert fn(None, p, p, p, p, p, p, ctypes.byref(idx), p, p, None, None) == 1
+    assert fn(ctypes.byref(small), None, p, p, p, p, p, ctypes.byref(idx), p, p, None, None) == 1
+    assert fn(ctypes.byref(small), p, p, p, p, p, p, None, p, p, None, None) == 1
+    bad = binding.make_config(configs.SMALL.with_(T=4100))
+    assert fn(ctypes.byref(bad), p, p, p, p, p, p, ctypes.byref(idx), p, p, None, None) == 2
+    assert lib.mono_workspace_bytes(ctypes.byref(big), binding.WS_ATTENTION) > \
+        binding.NOALLOC_SCRATCH_BYTES
+    assert fn(ctypes.byref(big), p, p, p, p, p, p, ctypes.byref(idx), p, p, None, None) == 6
+    assert b"scratch" in lib.mono_status_string(6)
