@@ -157,6 +157,36 @@ def run_gpu(cfg, steps, warmup, route_events=True):
     return wall_ms, stage, step_us, stats, sel
 
 
+def time_step_median(cfg, reps=3, warmup=1):
+    """The scaling study's protocol (technical report page, section
+    "Finite-range scaling": one warm-up, then three timed runs, the median):
+    `warmup` untimed steps, then `reps` steps each timed by its own HIP event
+    pair on the launch stream; returns (median ms, every timed ms)."""
+    import torch
+    from learned_sparse_causal_amd import binding, synth
+    d = synth.qkv_device(cfg)
+    cos, sin = binding.device_rope(cfg)
+    cb = torch.from_numpy(d["codebooks"]).cuda()
+    idx = binding.empty_index(cfg)
+    sel = torch.empty((cfg.B, cfg.Hq, cfg.T, cfg.R), dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.B, cfg.T, cfg.Hq, cfg.d), dtype=d["q"].dtype, device="cuda")
+    ws = torch.empty(max(1, binding.workspace_bytes(cfg, binding.WS_ATTENTION)), dtype=torch.uint8,
+                     device="cuda")
+    launch = binding.routed_attention_launcher(cfg, d["q"], d["k"], d["v"], cos, sin, cb, idx,
+                                               sel, out, ws)
+    for _ in range(warmup):
+        launch(None)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record()
+        launch(None)
+        e[1].record()
+        torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[1]) for e in ev]
+    return float(np.median(ms)), ms
+
+
 def time_dense(cfg, reps=3, warmup=1):
     """mono_dense_attention on the same inputs as the routed step: median of
     `reps` calls timed with HIP events on the launch stream (ms)."""
@@ -446,14 +476,19 @@ def main():
     )
     routed_ms = {}
     if not args.no_sweep:
-        pts = []
+        # 1 warm-up + 3 separately timed steps per length, median (the
+        # protocol of the report page's scaling study), and the least-squares
+        # exponent of ln t on ln T
+        pts, runs = [], {}
         for T in configs.SWEEP_T:
-            _, st, _, _, _ = run_gpu(configs.sweep(T), 3, 1, route_events=False)
-            pts.append((T, st["step_gpu_us"] * 1e-3))
+            med, ms = time_step_median(configs.sweep(T))
+            pts.append((T, med))
+            runs[str(T)] = ms
         routed_ms.update(pts)
         x = np.log([p[0] for p in pts])
         y = np.log([p[1] for p in pts])
-        line["sweep"] = dict(points_ms={str(T): ms for T, ms in pts},
+        line["sweep"] = dict(points_ms={str(T): ms for T, ms in pts}, timed_runs_ms=runs,
+                             protocol="1 warm-up + 3 timed steps, median",
                              exponent=float(np.polyfit(x, y, 1)[0]))
     if not args.no_dense:
         # routed step (index build + route + attention) against dense causal
@@ -463,8 +498,7 @@ def main():
         for T in cmp_t:
             c = configs.sweep(T)
             if T not in routed_ms:
-                _, st, _, _, _ = run_gpu(c, 3, 1, route_events=False)
-                routed_ms[T] = st["step_gpu_us"] * 1e-3
+                routed_ms[T] = time_step_median(c)[0]
             dms = time_dense(c)
             pts[str(T)] = dict(routed_ms=routed_ms[T], dense_ms=dms,
                                dense_over_routed=dms / routed_ms[T],

@@ -42,11 +42,13 @@ class MonoIndex(ctypes.Structure):
 _lib = None
 
 
-def load_library(path=LIB_PATH):
-    """Load libmono.so; raises OSError if it is not built."""
+def load_library(path=None):
+    """Load libmono.so (the in-tree build, or the file the environment
+    variable MONO_LIBRARY names); raises OSError if it is not built."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("MONO_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise OSError("libmono.so is not built (run `python -m learned_sparse_causal_amd.build`)")
     # torch first: the library then binds to the HIP runtime torch loaded, so

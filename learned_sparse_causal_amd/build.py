@@ -66,5 +66,43 @@ def build(verbose=False, incremental=False):
     return OUT
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C ABI
+# layer (argument validation, workspace layout, dispatch), for the sanitizer
+# run of the host tests.  Only the host pass of capi.cpp is instrumented (each
+# sanitizer flag applies to the host through -Xarch_host); the kernels' objects
+# are the normal build's.  Loaded through MONO_LIBRARY with clang's ASan runtime
+# preloaded.
+SAN_OUT = os.path.join(BUILD_DIR, "libmono_san.so")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime():
+    """clang's shared ASan runtime (it carries the UBSan handlers too)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_sanitized_host():
+    """Compile capi.cpp with host sanitizers and link it with the normal
+    build's kernel objects into _build/libmono_san.so."""
+    objs = [os.path.join(BUILD_DIR, src + ".o") for src in SOURCES if src != "capi.cpp"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError("build the library first: %s" % missing[0])
+    san_obj = os.path.join(BUILD_DIR, "capi_san.o")
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"]
+    subprocess.run(["hipcc", *flags, *SAN_HOST, "-x", "hip", "-c",
+                    os.path.join(CSRC, "capi.cpp"), "-o", san_obj],
+                   check=True, capture_output=True, text=True)
+    tmp = SAN_OUT + ".tmp%d" % os.getpid()
+    subprocess.run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *SAN_HOST,
+                    "-Xarch_host", "-shared-libsan", "-o", tmp, san_obj, *objs],
+                   check=True, capture_output=True, text=True)
+    os.replace(tmp, SAN_OUT)
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose=True, incremental="--incremental" in sys.argv[1:]))

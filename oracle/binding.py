@@ -13,19 +13,36 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source, for
+# the sanitizer run of the CPU tests: loaded instead of _LIB when the
+# environment sets ORACLE_SANITIZED=1 (the process must then preload gcc's
+# libasan, since the Python interpreter itself is not instrumented).
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g", "-O1"]
 _lib = None
 
 
-def build_oracle(force=True):
-    """Compile oracle.c with gcc (fp contraction off, OpenMP)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
-        return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+def _lib_path():
+    return _LIB_SAN if os.environ.get("ORACLE_SANITIZED") == "1" else _LIB
+
+
+def build_oracle(force=True, sanitize=None):
+    """Compile oracle.c with gcc (fp contraction off, OpenMP); with
+    sanitize=True (default: as ORACLE_SANITIZED asks) the instrumented
+    library."""
+    if sanitize is None:
+        sanitize = os.environ.get("ORACLE_SANITIZED") == "1"
+    lib = _LIB_SAN if sanitize else _LIB
+    if not force and os.path.exists(lib) and os.path.getmtime(lib) >= os.path.getmtime(_SRC):
+        return lib
+    tmp = lib + ".tmp%d" % os.getpid()
+    opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
            "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
     subprocess.check_call(cmd)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 class Shape(ctypes.Structure):
@@ -45,7 +62,7 @@ def load():
     global _lib
     if _lib is None:
         build_oracle(force=False)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(_lib_path())
         P = ctypes.c_void_p
         I = ctypes.c_int
         L = ctypes.c_long
