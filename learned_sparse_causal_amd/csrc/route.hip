@@ -1004,11 +1004,23 @@ size_t route_lds(const Shape &s, int waves, bool mf) {
            (size_t)waves * route_wave_floats(PK, s.ds, mf) * sizeof(float);
 }
 
-// Four waves per workgroup unless that overflows the 160 KiB of LDS.
+// Waves per workgroup: the count that puts the most waves on a compute unit
+// (at most eight, two per SIMD: the register cap), larger workgroups first.
+// Each wave's score area is about 17 KiB, so when the lists grow (2048
+// addresses or blocks and more) four-wave workgroups no longer fit twice in
+// the 160 KiB of LDS, and three-wave ones do.
 int route_waves(const Shape &s, bool mf) {
-    int w = 4;
-    while (w > 1 && route_lds(s, w, mf) > 160 * 1024) w /= 2;
-    return w;
+    int best = 1, best_waves = 0;
+    for (int w = 4; w >= 1; --w) {
+        const size_t lds = route_lds(s, w, mf);
+        if (lds > 160 * 1024) continue;
+        const int per_cu = std::min(8, (int)((160 * 1024) / lds) * w);
+        if (per_cu > best_waves) {
+            best = w;
+            best_waves = per_cu;
+        }
+    }
+    return best;
 }
 
 template <int D, int P, int NPRM, int RM, bool BF16, bool MF>
