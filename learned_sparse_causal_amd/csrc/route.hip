@@ -64,6 +64,11 @@ __device__ __forceinline__ u64 key_of(float s, uint32_t low_rank) {
     return ((u64)ordered(s) << 32) | (u64)low_rank;
 }
 
+__device__ __forceinline__ u64 shfl_xor_u64(u64 v, int off) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off), hi = __shfl_xor((uint32_t)(v >> 32), off);
+    return ((u64)hi << 32) | lo;
+}
+
 template <int M>
 __device__ __forceinline__ void insert(u64 (&lst)[M], u64 k) {
 #pragma unroll
@@ -804,26 +809,87 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
             }
         };
         if constexpr (RM == 2) {
-            scan([&](const float (&sg)[U], int i0) { batch_vals(sg, i0 / U); });
-            // the first entry of a batch whose sigma equals val, other than excl
-            auto find = [&](int batch, float val, int excl) {
-                int res = -1;
-                if (batch >= 0) {
+            // the list positions of the best and second best entries
+            int first = -1, second = -1;
+            const u64 needm = __ballot(need);
+            const int nneed = __popcll(needm);
+            if (PK <= WAVE && nneed <= 6 && nneed * ((nal + WAVE - 1) / WAVE * 12 + 100) < nal * 8) {
+                // Few lanes need the extension (long lists late in long
+                // sequences): the whole wave scans the list once per such
+                // lane.  Lane c holds that query's score of code row c, each
+                // lane takes every 64th entry and keeps its two best
+                // (sigma, position) keys, and a butterfly of merges gives
+                // the wave's two best.  Keys order by sigma, then by lower
+                // position, i.e. lower address: the single-lane scan's order.
+                // The rule is wave-uniform and picks the cheaper form by its
+                // instruction count (about 12 per entry and lane plus 100 per
+                // needing lane, against 8 per entry).
+                u64 mm = needm;
+                while (mm) {
+                    const int j = __ffsll((long long)mm) - 1;     // wave-uniform
+                    mm &= mm - 1;
+                    const float sj = lane < PK ? sc_s[lane * SROW + j] : -INFINITY;
+                    u64 k0 = 0ull, k1 = 0ull;
+                    constexpr int CU4 = 4;   // entries per lane in flight
+                    for (int e0 = 0; e0 < nal; e0 += CU4 * WAVE) {
+                        int2 m[CU4];
+                        float sg[CU4];
 #pragma unroll
-                    for (int u = U - 1; u >= 0; --u) {
-                        const int i = batch * U + u;
-                        const bool hit = i < nal && i != excl && sigma(alist[i]) == val;
-                        res = hit ? i : res;
+                        for (int u = 0; u < CU4; ++u) {
+                            const int e = e0 + u * WAVE + lane;
+                            m[u] = alist[e < nal ? e : 0];
+                        }
+#pragma unroll
+                        for (int u = 0; u < CU4; ++u) {
+                            const float a = __shfl(sj, m[u].x / (SROW * 4));
+                            const float c = P == 1 ? 0.0f : __shfl(sj, m[u].y / (SROW * 4));
+                            sg[u] = P == 1 ? a : a + c;
+                        }
+#pragma unroll
+                        for (int u = 0; u < CU4; ++u) {
+                            const int e = e0 + u * WAVE + lane;
+                            const u64 key = e < nal ? key_of(sg[u], (uint32_t)(0x7FFFFFFF - e)) : 0ull;
+                            const bool b0 = key > k0;
+                            k1 = b0 ? k0 : (key > k1 ? key : k1);
+                            k0 = b0 ? key : k0;
+                        }
+                    }
+#pragma unroll
+                    for (int off = WAVE / 2; off > 0; off >>= 1) {
+                        const u64 p0 = shfl_xor_u64(k0, off), p1 = shfl_xor_u64(k1, off);
+                        const u64 hi = k0 > p0 ? k0 : p0, lo = k0 > p0 ? p0 : k0;
+                        const u64 m1 = k1 > p1 ? k1 : p1;
+                        k1 = lo > m1 ? lo : m1;
+                        k0 = hi;
+                    }
+                    if (lane == j) {
+                        first = k0 ? 0x7FFFFFFF - (int)(k0 & 0xFFFFFFFFu) : -1;
+                        second = (R == 2 && k1) ? 0x7FFFFFFF - (int)(k1 & 0xFFFFFFFFu) : -1;
                     }
                 }
-                return res;
-            };
-            const int i0 = RM - R == 0 && v0 > -INFINITY ? find(bb0, v0, -1) : -1;
-            const int i1 = v1 > -INFINITY ? find(bb1, v1, i0) : -1;
-            const u64 k0 = i0 >= 0 ? addr_key(v0, addr_of(alist[i0])) : 0ull;
-            const u64 k1 = i1 >= 0 ? addr_key(v1, addr_of(alist[i1])) : 0ull;
-            top[0] = RM - R == 0 ? k0 : k1;
-            top[1] = RM - R == 0 ? k1 : 0ull;
+            } else {
+                scan([&](const float (&sg)[U], int i0) { batch_vals(sg, i0 / U); });
+                // the first entry of a batch whose sigma equals val, other than excl
+                auto find = [&](int batch, float val, int excl) {
+                    int res = -1;
+                    if (batch >= 0) {
+#pragma unroll
+                        for (int u = U - 1; u >= 0; --u) {
+                            const int i = batch * U + u;
+                            const bool hit = i < nal && i != excl && sigma(alist[i]) == val;
+                            res = hit ? i : res;
+                        }
+                    }
+                    return res;
+                };
+                const int i0 = RM - R == 0 && v0 > -INFINITY ? find(bb0, v0, -1) : -1;
+                const int i1 = v1 > -INFINITY ? find(bb1, v1, i0) : -1;
+                // with one slot (R = 1) slot 1 holds the best
+                first = RM - R == 0 ? i0 : i1;
+                second = RM - R == 0 ? i1 : -1;
+            }
+            top[0] = first >= 0 ? addr_key(sigma(alist[first]), addr_of(alist[first])) : 0ull;
+            top[1] = second >= 0 ? addr_key(sigma(alist[second]), addr_of(alist[second])) : 0ull;
         } else {
             scan([&](const float (&sg)[U], int) {
 #pragma unroll

@@ -1,7 +1,7 @@
 """Every point of the scaling sweep (4K, 8K, 16K and 32K tokens), run as the
 whole step in one call (mono_routed_attention, the call the benchmark times)
 and checked against the oracle, as the technical report's section
-"Finite-range scaling" checks each of its lengths: the whole index (block
+"Finite-range scaling" checks each of its lengths (and at 64K tokens): the whole index (block
 summaries, addresses, lists, loads and counters) bit for bit with zero
 overflow; sampled routes bit for bit (near-ties excused under the 0.01 %
 cap) with the causality and fixed-slot checks on every route; sampled
@@ -16,7 +16,10 @@ from parity import (check_attention, check_sel_invariants, compare_index, compar
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T", configs.SWEEP_T)
+# the four sweep lengths, and 64K tokens (the comparison's longest length;
+# late query blocks there leave few lanes needing the extension, so the
+# router's wave-cooperative extension runs)
+@pytest.mark.parametrize("T", configs.SWEEP_T + (65536,))
 def test_sweep_point_whole_step(orc, T):
     cfg = configs.sweep(T)
     say("[sweep] %s" % cfg.name)
