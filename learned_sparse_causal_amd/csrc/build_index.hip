@@ -13,11 +13,14 @@
 //   defined), so the summary is bit-identical to a sequential evaluation.
 //   Code scores are fp32 fused multiply-add chains in dimension order; the
 //   argmax keeps the lowest code on ties.  HBM-bound: the keys are read once.
-// k_posting_lists: one workgroup per (batch, kv-head).  LDS histogram,
-//   exclusive scan of the clamped counts, then a stable rank of every block
-//   within its address from wavefront ballots over the address bits (chunks
-//   of 64 blocks in source order, running per-address counts in LDS), and a
-//   scatter that keeps the first `cap` blocks of every list.
+// k_posting_lists: one workgroup per (batch, kv-head), each of its waves
+//   owning a contiguous range of blocks.  Counts per (range, address) give
+//   the loads and, by a prefix over the ranges, where each range's blocks of
+//   an address start; an exclusive scan of the clamped loads gives the list
+//   starts; then every wave ranks its own blocks within their address from
+//   wavefront ballots over the address bits (chunks of 64 blocks in source
+//   order, running per-address counts in LDS), so the ranking runs on all
+//   waves at once, and the first `cap` blocks of every list are placed.
 #include "common.hpp"
 
 namespace {
@@ -220,9 +223,17 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
 }
 
 constexpr int PL_THREADS = 256;
+constexpr int PL_WAVES = PL_THREADS / WAVE;
 
 // nbu: blocks 0 .. nbu-1 are indexed (NB for a whole sequence); arrays keep
-// their NB strides.
+// their NB strides.  Wave w owns the contiguous block range
+// [w * span, (w + 1) * span) (span a multiple of 64); LDS:
+//   hist  [A]            loads (blocks per address, before the clamp)
+//   off   [A + 1]        list starts (exclusive scan of min(load, cap))
+//   cnt   [PL_WAVES][A]  blocks of each address in each wave's range, then
+//                        the count in the earlier ranges (exclusive prefix
+//                        over waves) and, while ranking, the running count
+//   adr   [nbu]          the addresses
 __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
                                                               const int32_t *__restrict__ addr,
                                                               int32_t *__restrict__ offsets,
@@ -231,28 +242,43 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
                                                               int32_t *__restrict__ overflow) {
     extern __shared__ int32_t lds[];
     const int A = s.A, NB = s.NB, cap = s.cap;
-    int32_t *hist = lds;            // [A] loads
-    int32_t *off = lds + A;         // [A+1] list starts
-    int32_t *run = lds + 2 * A + 1; // [A] blocks already placed per address
-    int32_t *adr = lds + 3 * A + 1; // [nbu] the addresses, for the ranking pass
-    __shared__ int32_t part[PL_THREADS / WAVE];
-    __shared__ int32_t ovf_s[PL_THREADS / WAVE];
+    int32_t *hist = lds;
+    int32_t *off = lds + A;
+    int32_t *cnt = lds + 2 * A + 1;
+    int32_t *adr = lds + (2 + PL_WAVES) * A + 1;
+    __shared__ int32_t part[PL_WAVES];
+    __shared__ int32_t ovf_s[PL_WAVES];
 
     const int u = blockIdx.x;  // b * Hkv + g
     const int32_t *ad = addr + (size_t)u * NB;
-    const int tid = threadIdx.x;
-    for (int a = tid; a < A; a += PL_THREADS) { hist[a] = 0; run[a] = 0; }
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+    const int span = ((nbu + PL_WAVES - 1) / PL_WAVES + WAVE - 1) / WAVE * WAVE;
+    for (int i = tid; i < PL_WAVES * A; i += PL_THREADS) cnt[i] = 0;
+    for (int n = tid; n < nbu; n += PL_THREADS) adr[n] = ad[n];
     __syncthreads();
-    for (int n = tid; n < nbu; n += PL_THREADS) {
-        const int a = ad[n];
-        adr[n] = a;
-        atomicAdd(&hist[a], 1);
+    // pass 1: counts per (wave range, address)
+    {
+        int32_t *cw = cnt + wv * A;
+        const int n0 = wv * span, n1 = min(nbu, n0 + span);
+        for (int n = n0 + lane; n < n1; n += WAVE) atomicAdd(&cw[adr[n]], 1);
+    }
+    __syncthreads();
+    // per address: exclusive prefix over the wave ranges, total load
+    for (int a = tid; a < A; a += PL_THREADS) {
+        int acc = 0;
+#pragma unroll
+        for (int w = 0; w < PL_WAVES; ++w) {
+            const int c = cnt[w * A + a];
+            cnt[w * A + a] = acc;
+            acc += c;
+        }
+        hist[a] = acc;
     }
     __syncthreads();
 
     // exclusive scan of min(load, cap): each thread owns a contiguous chunk
     const int per = (A + PL_THREADS - 1) / PL_THREADS;
-    const int lo = tid * per, hi = min(A, lo + per);
+    const int lo = min(A, tid * per), hi = min(A, lo + per);
     int sum = 0, ov = 0;
     for (int a = lo; a < hi; ++a) {
         const int l = hist[a];
@@ -260,8 +286,7 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
         ov += max(0, l - cap);
     }
     // block-wide exclusive scan of the per-thread sums: wave prefix by
-    // shuffles, then the four wave totals
-    const int lane = tid & (WAVE - 1), wv = tid / WAVE;
+    // shuffles, then the wave totals
     int incl = sum;
 #pragma unroll
     for (int dlt = 1; dlt < WAVE; dlt <<= 1) {
@@ -276,7 +301,7 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
     __syncthreads();
     int wbase = 0, total_all = 0, ovf_all = 0;
 #pragma unroll
-    for (int w = 0; w < PL_THREADS / WAVE; ++w) {
+    for (int w = 0; w < PL_WAVES; ++w) {
         const int v = part[w];
         wbase += w < wv ? v : 0;
         total_all += v;
@@ -302,14 +327,20 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
     const int total = off[A];
     for (int x = total + tid; x < NB; x += PL_THREADS) ent_g[x] = -1;
 
-    // stable ranks: wave 0 walks the blocks in source order, 64 at a time
-    if (tid < WAVE) {
+    // pass 2: stable ranks.  Each wave walks its range in source order, 64
+    // blocks at a time; lanes of equal address find each other with one
+    // ballot per address bit, rank by their lane order after the blocks of
+    // that address in earlier ranges and earlier chunks (the running count),
+    // and the first `cap` of every address are placed.
+    {
         int nbits = 0;
         while ((1 << nbits) < A) ++nbits;
-        const uint64_t lt = (1ull << tid) - 1ull;
-        for (int c0 = 0; c0 < nbu; c0 += WAVE) {
-            const int n = c0 + tid;
-            const bool in = n < nbu;
+        const uint64_t lt = (1ull << lane) - 1ull;
+        int32_t *run = cnt + wv * A;
+        const int n0 = wv * span, n1 = min(nbu, n0 + span);
+        for (int c0 = n0; c0 < n1; c0 += WAVE) {
+            const int n = c0 + lane;
+            const bool in = n < n1;
             const int a = in ? adr[n] : 0;
             uint64_t m = __ballot(in);
             for (int bit = 0; bit < nbits; ++bit) {
@@ -320,7 +351,7 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
             if (in) rank = run[a] + __popcll(m & lt);
             __builtin_amdgcn_wave_barrier();
             // the highest lane of each group advances the running count
-            if (in && (m >> tid) == 1ull) run[a] += __popcll(m);
+            if (in && (m >> lane) == 1ull) run[a] += __popcll(m);
             __builtin_amdgcn_wave_barrier();
             if (in && rank < cap) ent_g[off[a] + rank] = n;
         }
@@ -385,7 +416,7 @@ hipError_t launch_block_address(const Shape &s, const void *k, const float *cos_
 hipError_t launch_posting_lists_prefix(const Shape &s, int nbu, const int32_t *addr,
                                        int32_t *offsets, int32_t *entries, int32_t *load,
                                        int32_t *overflow, hipStream_t st) {
-    const size_t lds = (size_t)(3 * s.A + 1 + nbu) * sizeof(int32_t);
+    const size_t lds = (size_t)((2 + PL_WAVES) * s.A + 1 + nbu) * sizeof(int32_t);
     const hipError_t e = mono_lds_limit(reinterpret_cast<const void *>(k_posting_lists), lds);
     if (e != hipSuccess) return e;
     k_posting_lists<<<dim3(s.B * s.Hkv), PL_THREADS, lds, st>>>(s, nbu, addr, offsets, entries,
