@@ -7,12 +7,16 @@
 // decision per code component; the address selects a capacity-bounded causal
 // posting list; overflow is counted; the build is a stable sort.
 //
-// k_block_address: one rotation pair (dims i, i + d/2) per lane; each lane
+// k_block_address: one workgroup per (batch, block, group of kv-heads), one
+//   rotation pair (dims i, i + d/2 of one kv-head) per thread; each thread
 //   rotates and sums its two dimensions over the block's tokens in token
 //   order (fp32, products rounded before the add, as the rotation is
 //   defined), so the summary is bit-identical to a sequential evaluation.
 //   Code scores are fp32 fused multiply-add chains in dimension order; the
 //   argmax keeps the lowest code on ties.  HBM-bound: the keys are read once.
+//   Every step is independent per kv-head, so splitting the heads over
+//   workgroups shortens each workgroup's chain of chunk loads and gives the
+//   chip more workgroups to overlap.
 // k_posting_lists: one workgroup per (batch, kv-head), each of its waves
 //   owning a contiguous range of blocks.  Counts per (range, address) give
 //   the loads and, by a prefix over the ranges, where each range's blocks of
@@ -26,39 +30,50 @@
 namespace {
 
 constexpr int BA_THREADS = 256;
-constexpr int BA_CHUNK_BYTES = 32768;   // LDS staging of key rows per chunk
+constexpr int BA_CHUNK_BYTES = 16384;   // LDS staging of key rows per chunk
+constexpr int BA_UB = 8;                // tokens read together per summing step (divides every chunk)
+
+// kv-heads per workgroup: the largest power of two dividing Hkv whose
+// rotation pairs fit one per thread.
+int block_head_group(const Shape &s) {
+    int hg = 1;
+    while (s.Hkv % (2 * hg) == 0 && 2 * hg * (s.d / 2) <= BA_THREADS) hg *= 2;
+    return hg;
+}
 
 // Tokens per staged chunk: the largest power of two dividing the block size
-// whose rows (all kv-heads) fit in BA_CHUNK_BYTES and whose rotary-table
+// whose rows (hg kv-heads) fit in BA_CHUNK_BYTES and whose rotary-table
 // entries (d/2 per token) fit the per-thread staging registers.
-int block_chunk_tokens(const Shape &s) {
-    const int row = s.Hkv * s.d * (s.dtype == 1 ? 2 : 4);
+int block_chunk_tokens(const Shape &s, int hg) {
+    const int row = hg * s.d * (s.dtype == 1 ? 2 : 4);
     const int tab_max = BA_CHUNK_BYTES / 16;     // VPT * BA_THREADS
     int ct = s.beta;
     while (ct > 1 && (ct * row > BA_CHUNK_BYTES || ct * (s.d / 2) > tab_max)) ct /= 2;
     return ct;
 }
 
-size_t block_address_lds(const Shape &s, int ct) {
+size_t block_address_lds(const Shape &s, int ct, int hg) {
     const int es = s.dtype == 1 ? 2 : 4;
-    return (size_t)ct * s.Hkv * s.d * es          // key rows
+    return (size_t)ct * hg * s.d * es             // key rows
            + (size_t)2 * ct * (s.d / 2) * 4       // cos, sin rows
-           + (size_t)s.Hkv * s.d * 4              // summaries
-           + (size_t)s.Hkv * s.P * s.K * 4;       // code scores
+           + (size_t)hg * s.d * 4                 // summaries
+           + (size_t)hg * s.P * s.K * 4;          // code scores
 }
 
-// One workgroup per (batch, block n).  The block's key rows (every kv-head)
-// pass through LDS in chunks of CT tokens, read with 16-byte loads; the next
-// chunk's loads are in flight while the current chunk is summed.  Thread slot
-// j of thread x owns rotation pair x + 256 j, i.e. kv-head g and dims
+// One workgroup per (batch, block n, kv-heads HG z .. HG z + HG - 1).  The
+// block's key rows of those heads pass through LDS in chunks of CT tokens,
+// read with 16-byte loads (VSH = log2 of the 16-byte vectors per token row);
+// the next chunk's loads are in flight while the current chunk is summed.
+// Thread x owns rotation pair x, i.e. kv-head g0 + x / (d/2) and dims
 // (i, i + d/2), and sums it over the tokens in order (fp32, products rounded
 // before the add, as the rotation is defined).  Then one thread per
 // (kv-head, code) scores the summary with an fp32 fused multiply-add chain
 // in dimension order and one thread per kv-head takes the argmax of every
 // component (lowest code on ties) and writes the address.  MAXP bounds the
-// pairs per thread (Hkv d / 2 <= 256 MAXP).
-template <int D, int P, bool BF16, int MAXP>
-__global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, int n0,
+// pairs per thread (HG d / 2 <= 256 MAXP).
+template <int D, int P, bool BF16, int MAXP, bool ROT>
+__global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, int HG, int VSH,
+                                                              int n0,
                                                               const void *__restrict__ k,
                                                               const float *__restrict__ cos_t,
                                                               const float *__restrict__ sin_t,
@@ -72,20 +87,25 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
     constexpr int VPT = BA_CHUNK_BYTES / 16 / BA_THREADS;      // 16-byte loads per thread
     extern __shared__ __align__(16) char ba_lds[];
     const int Hkv = s.Hkv, K = s.K, PK = P * K;
-    const int rowE = Hkv * D;                                   // elements per token row
+    const int rowE = HG * D;                                    // elements per staged token row
+    const size_t growB = (size_t)Hkv * D * ES;                  // bytes per global token row
     char *rows = ba_lds;                                        // [CT][rowE]
     float *cs = reinterpret_cast<float *>(ba_lds + (size_t)CT * rowE * ES);   // [CT][H]
     float *sn = cs + CT * H;                                    // [CT][H]
-    float *kb = sn + CT * H;                                    // [Hkv][D]
-    float *sc = kb + Hkv * D;                                   // [Hkv][PK]
+    float *kb = sn + CT * H;                                    // [HG][D]
+    float *sc = kb + HG * D;                                    // [HG][PK]
 
     const int tid = threadIdx.x;
-    const int n = n0 + blockIdx.x, b = blockIdx.y;
+    const int n = n0 + blockIdx.x, b = blockIdx.y, g0 = blockIdx.z * HG;
     const int t0 = n * s.beta;
-    const int npairs = Hkv * H;
-    const int vecs = CT * rowE * ES / 16;                       // 16-byte vectors per chunk
+    const int npairs = HG * H;
+    const int vecs = CT << VSH;                                 // 16-byte vectors per chunk
+    const int vmask = (1 << VSH) - 1;
     const int tabs = CT * H;                                    // table entries per chunk
-    const char *kbase = reinterpret_cast<const char *>(k) + ((size_t)b * s.T + t0) * rowE * ES;
+    const char *kbase = reinterpret_cast<const char *>(k) + ((size_t)b * s.T + t0) * growB +
+                        (size_t)g0 * D * ES;
+    // byte offset of staged vector v (token v >> VSH, vector v & vmask of its row)
+    auto goff = [&](int v) { return (size_t)(v >> VSH) * growB + (size_t)(v & vmask) * 16; };
 
     float a0[MAXP], a1[MAXP];
 #pragma unroll
@@ -97,18 +117,17 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
     float tc[VPT], ts[VPT];
 #define MONO_BA_FETCH(c_)                                                                  \
     {                                                                                      \
-        const u32x4 *src_ = reinterpret_cast<const u32x4 *>(kbase + (size_t)(c_)*rowE * ES); \
+        const char *src_ = kbase + (size_t)(c_)*growB;                                     \
         const float *cg_ = cos_t + (size_t)(t0 + (c_)) * H;                                \
         const float *sg_ = sin_t + (size_t)(t0 + (c_)) * H;                                \
         _Pragma("clang loop unroll(full)") for (int j = 0; j < VPT; ++j) {                  \
             const int v = tid + j * BA_THREADS;                                            \
-            tmp[j] = src_[min(v, vecs - 1)];                                               \
+            tmp[j] = *reinterpret_cast<const u32x4 *>(src_ + goff(min(v, vecs - 1)));      \
             tc[j] = cg_[min(v, tabs - 1)];                                                 \
             ts[j] = sg_[min(v, tabs - 1)];                                                 \
         }                                                                                  \
     }
-    MONO_BA_FETCH(0)
-    for (int c = 0; c < s.beta; c += CT) {
+    auto stage = [&]() {
 #pragma clang loop unroll(full)
         for (int j = 0; j < VPT; ++j) {
             const int v = tid + j * BA_THREADS;
@@ -119,47 +138,83 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
             const int v = tid + j * BA_THREADS;
             if (v < tabs) { cs[v] = tc[j]; sn[v] = ts[j]; }
         }
-        __syncthreads();
-        if (c + CT < s.beta) MONO_BA_FETCH(c + CT)
+    };
+    MONO_BA_FETCH(0)
+    stage();
+    __syncthreads();
+    for (int c = 0; c < s.beta; c += CT) {
+        const bool more = c + CT < s.beta;
+        if (more) MONO_BA_FETCH(c + CT)
 #pragma unroll
         for (int j = 0; j < MAXP; ++j) {
             const int pr = tid + j * BA_THREADS;
             if (pr < npairs) {
                 const int g = pr / H, i = pr - g * H;
-#pragma unroll 8
-                for (int u = 0; u < CT; ++u) {
-                    const int e = u * rowE + g * D + i;
-                    float x0, x1;
-                    if constexpr (BF16) {
-                        x0 = bf16_bits_to_f32(reinterpret_cast<const u16 *>(rows)[e]);
-                        x1 = bf16_bits_to_f32(reinterpret_cast<const u16 *>(rows)[e + H]);
-                    } else {
-                        x0 = reinterpret_cast<const float *>(rows)[e];
-                        x1 = reinterpret_cast<const float *>(rows)[e + H];
-                    }
-                    const float cc = cs[u * H + i], ss = sn[u * H + i];
-                    const float p0 = x0 * cc, p1 = x1 * ss, p2 = x1 * cc, p3 = x0 * ss;
-                    const float r0 = p0 - p1, r1 = p2 + p3;
-                    a0[j] = a0[j] + r0;
-                    a1[j] = a1[j] + r1;
-                    if (k_rot) {   // the rotated pair replaces the staged one (this thread's)
+                const int e0 = g * D + i;
+                // BA_UB tokens at a time: their staged values and table
+                // entries are read together, then summed in token order
+                for (int u0 = 0; u0 < CT; u0 += BA_UB) {
+                    float x0[BA_UB], x1[BA_UB], cc[BA_UB], ss[BA_UB];
+#pragma unroll
+                    for (int v = 0; v < BA_UB; ++v) {
+                        const int e = (u0 + v) * rowE + e0;
                         if constexpr (BF16) {
-                            reinterpret_cast<u16 *>(rows)[e] = f32_to_bf16_bits(r0);
-                            reinterpret_cast<u16 *>(rows)[e + H] = f32_to_bf16_bits(r1);
+                            x0[v] = bf16_bits_to_f32(reinterpret_cast<const u16 *>(rows)[e]);
+                            x1[v] = bf16_bits_to_f32(reinterpret_cast<const u16 *>(rows)[e + H]);
                         } else {
-                            reinterpret_cast<float *>(rows)[e] = r0;
-                            reinterpret_cast<float *>(rows)[e + H] = r1;
+                            x0[v] = reinterpret_cast<const float *>(rows)[e];
+                            x1[v] = reinterpret_cast<const float *>(rows)[e + H];
+                        }
+                        cc[v] = cs[(u0 + v) * H + i];
+                        ss[v] = sn[(u0 + v) * H + i];
+                    }
+                    float r0[BA_UB], r1[BA_UB];
+#pragma unroll
+                    for (int v = 0; v < BA_UB; ++v) {
+                        const float p0 = x0[v] * cc[v], p1 = x1[v] * ss[v];
+                        const float p2 = x1[v] * cc[v], p3 = x0[v] * ss[v];
+                        r0[v] = p0 - p1;
+                        r1[v] = p2 + p3;
+                        a0[j] = a0[j] + r0[v];
+                        a1[j] = a1[j] + r1[v];
+                    }
+                    if constexpr (ROT) {   // the rotated pairs replace the staged ones (this thread's)
+#pragma unroll
+                        for (int v = 0; v < BA_UB; ++v) {
+                            const int e = (u0 + v) * rowE + e0;
+                            if constexpr (BF16) {
+                                reinterpret_cast<u16 *>(rows)[e] = f32_to_bf16_bits(r0[v]);
+                                reinterpret_cast<u16 *>(rows)[e + H] = f32_to_bf16_bits(r1[v]);
+                            } else {
+                                reinterpret_cast<float *>(rows)[e] = r0[v];
+                                reinterpret_cast<float *>(rows)[e + H] = r1[v];
+                            }
                         }
                     }
                 }
             }
         }
         __syncthreads();
-        if (k_rot) {   // the chunk's rotated rows, rounded to the activation dtype
-            u32x4 *dst = reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(k_rot) +
-                                                   ((size_t)b * s.T + t0 + c) * rowE * ES);
-            for (int v = tid; v < vecs; v += BA_THREADS) dst[v] = reinterpret_cast<const u32x4 *>(rows)[v];
-            __syncthreads();   // read before the next chunk overwrites the rows
+        if constexpr (ROT) {
+            // the chunk's rotated rows, rounded to the activation dtype: a
+            // fixed number of stores per thread (indexes clamped; a clamped
+            // store rewrites the last vector with its own value), so that
+            // the wait for the next chunk's loads below does not also wait
+            // for these stores to complete
+            char *dst = reinterpret_cast<char *>(k_rot) + ((size_t)b * s.T + t0 + c) * growB +
+                        (size_t)g0 * D * ES;
+            u32x4 out[VPT];
+#pragma clang loop unroll(full)
+            for (int j = 0; j < VPT; ++j)
+                out[j] = reinterpret_cast<const u32x4 *>(rows)[min(tid + j * BA_THREADS, vecs - 1)];
+#pragma clang loop unroll(full)
+            for (int j = 0; j < VPT; ++j)
+                *reinterpret_cast<u32x4 *>(dst + goff(min(tid + j * BA_THREADS, vecs - 1))) = out[j];
+            if (more) __syncthreads();   // read before the next chunk overwrites the rows
+        }
+        if (more) {
+            stage();
+            __syncthreads();
         }
     }
 #undef MONO_BA_FETCH
@@ -174,7 +229,7 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
             const float kb0 = a0[j] * inv_beta, kb1 = a1[j] * inv_beta;
             kb[g * D + i] = kb0;
             kb[g * D + i + H] = kb1;
-            float *dst = kbar + (((size_t)b * Hkv + g) * s.NB + n) * D;
+            float *dst = kbar + (((size_t)b * Hkv + g0 + g) * s.NB + n) * D;
             dst[i] = kb0;
             dst[i + H] = kb1;
         }
@@ -183,9 +238,10 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
 
     // code scores: thread per (kv-head, component code); the code row is
     // loaded whole before the chain starts
-    for (int x = tid; x < Hkv * PK; x += BA_THREADS) {
+    for (int x = tid; x < HG * PK; x += BA_THREADS) {
         const int g = x / PK, code = x - g * PK, p = code / K;
-        const float4 *crow = reinterpret_cast<const float4 *>(cb + ((size_t)g * PK + code) * DS);
+        const float4 *crow =
+            reinterpret_cast<const float4 *>(cb + ((size_t)(g0 + g) * PK + code) * DS);
         float4 cv[DS / 4];
 #pragma unroll
         for (int j = 0; j < DS / 4; ++j) cv[j] = crow[j];
@@ -203,7 +259,7 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
     __syncthreads();
 
     // argmax per component (lowest code on ties), address = mixed radix
-    for (int g = tid; g < Hkv; g += BA_THREADS) {
+    for (int g = tid; g < HG; g += BA_THREADS) {
         int a = 0;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
@@ -218,7 +274,7 @@ __global__ __launch_bounds__(BA_THREADS) void k_block_address(Shape s, int CT, i
             }
             a = a * K + best;
         }
-        addr[((size_t)b * Hkv + g) * s.NB + n] = a;
+        addr[((size_t)b * Hkv + g0 + g) * s.NB + n] = a;
     }
 }
 
@@ -359,16 +415,18 @@ __global__ __launch_bounds__(PL_THREADS) void k_posting_lists(Shape s, int nbu,
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, int P, bool BF16, int MAXP>
-hipError_t launch_ba_t(const Shape &s, int n0, int n1, int ct, size_t lds, const void *k,
+template <int D, int P, bool BF16>
+hipError_t launch_ba_t(const Shape &s, int n0, int n1, int ct, int hg, size_t lds, const void *k,
                        const float *cos_t, const float *sin_t, const float *cb, float *kbar,
                        int32_t *addr, void *k_rot, hipStream_t st) {
-    auto *fn = k_block_address<D, P, BF16, MAXP>;
+    // hg d / 2 <= 256 pairs: one per thread
+    auto *fn = k_rot ? k_block_address<D, P, BF16, 1, true> : k_block_address<D, P, BF16, 1, false>;
     const hipError_t e = mono_lds_limit(reinterpret_cast<const void *>(fn), lds);
     if (e != hipSuccess) return e;
-    fn<<<dim3((unsigned)(n1 - n0), (unsigned)s.B), BA_THREADS, lds, st>>>(s, ct, n0, k, cos_t,
-                                                                          sin_t, cb, kbar, addr,
-                                                                          k_rot);
+    int vsh = 0;   // 16-byte vectors per staged token row: hg d es / 16, a power of two
+    while ((16 << vsh) < hg * D * (BF16 ? 2 : 4)) ++vsh;
+    fn<<<dim3((unsigned)(n1 - n0), (unsigned)s.B, (unsigned)(s.Hkv / hg)), BA_THREADS, lds, st>>>(
+        s, ct, hg, vsh, n0, k, cos_t, sin_t, cb, kbar, addr, k_rot);
     return hipGetLastError();
 }
 
@@ -376,16 +434,15 @@ template <int D, bool BF16>
 hipError_t launch_ba(const Shape &s, int n0, int n1, const void *k, const float *cos_t,
                      const float *sin_t, const float *cb, float *kbar, int32_t *addr,
                      void *k_rot, hipStream_t st) {
-    const int ct = block_chunk_tokens(s);
-    const size_t lds = block_address_lds(s, ct);
-    const bool small = s.Hkv * (D / 2) <= 2 * BA_THREADS;
-#define MONO_BA_ARGS s, n0, n1, ct, lds, k, cos_t, sin_t, cb, kbar, addr, k_rot, st
+    const int hg = block_head_group(s);
+    const int ct = block_chunk_tokens(s, hg);
+    if (ct % BA_UB) return hipErrorInvalidValue;   // not reached for d <= 128
+    const size_t lds = block_address_lds(s, ct, hg);
     if (s.P == 1)
-        return small ? launch_ba_t<D, 1, BF16, 2>(MONO_BA_ARGS)
-                     : launch_ba_t<D, 1, BF16, 8>(MONO_BA_ARGS);
-    return small ? launch_ba_t<D, 2, BF16, 2>(MONO_BA_ARGS)
-                 : launch_ba_t<D, 2, BF16, 8>(MONO_BA_ARGS);
-#undef MONO_BA_ARGS
+        return launch_ba_t<D, 1, BF16>(s, n0, n1, ct, hg, lds, k, cos_t, sin_t, cb, kbar, addr,
+                                       k_rot, st);
+    return launch_ba_t<D, 2, BF16>(s, n0, n1, ct, hg, lds, k, cos_t, sin_t, cb, kbar, addr, k_rot,
+                                   st);
 }
 
 }  // namespace

@@ -27,10 +27,15 @@
 //   in ascending order.
 // k_decode_attend: one workgroup per (batch, q-head).  The local blocks and
 //   the valid, first-occurrence selected blocks are split in 64-key items
-//   over eight waves; four lanes score one key (rotated in fp32 from the
-//   cache), each wave keeps an online softmax and accumulates P V with the
-//   64 value rows of an item loaded back to back, and the eight states are
-//   merged through LDS.
+//   over eight waves; four lanes score one key, each wave keeps an online
+//   softmax and accumulates P V with the 64 value rows of an item loaded back
+//   to back, and the eight states are merged through LDS.  Keys are rotated
+//   relative to their item's first position s0: a rotation by s is the
+//   rotation by s0 followed by the one by s - s0, so the score is the query
+//   rotated back by s0 against the key rotated by its offset in the item.
+//   The query's back-rotation is done once per item; the keys then read
+//   only the first 64 rows of the rotary table, which stay in the caches,
+//   instead of one row per key.
 #include <algorithm>
 #include <climits>
 
@@ -320,7 +325,7 @@ constexpr int DA_THREADS = 512;
 constexpr int DA_WAVES = DA_THREADS / WAVE;
 
 size_t decode_attend_lds(const Shape &s) {
-    return (size_t)(s.d + DA_WAVES * (WAVE + 2 + s.d)) * 4 + (size_t)(s.R + s.L) * 4;
+    return (size_t)(s.d + DA_WAVES * (WAVE + 2 + 2 * s.d)) * 4 + (size_t)(s.R + s.L) * 4;
 }
 
 // DPL consecutive elements starting at i, as floats.
@@ -354,7 +359,8 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
     float *pw = qr + D;                           // [DA_WAVES][WAVE] probabilities
     float *ml = pw + DA_WAVES * WAVE;             // [DA_WAVES][2] (m, l)
     float *ow = ml + DA_WAVES * 2;                // [DA_WAVES][D]
-    int *blk = reinterpret_cast<int *>(ow + DA_WAVES * D);   // [L + R]
+    float *qi = ow + DA_WAVES * D;                // [DA_WAVES][D] query rotated back by s0
+    int *blk = reinterpret_cast<int *>(qi + DA_WAVES * D);   // [L + R]
 
     const int route = blockIdx.x;
     const int b = route / s.Hq, h = route % s.Hq, g = h / s.G;
@@ -390,6 +396,7 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
     const size_t rs = (size_t)s.Hkv * D;          // cache row stride (elements)
     const size_t base = ((size_t)b * s.T * s.Hkv + g) * D;
     float *p_s = pw + wave * WAVE;
+    float *q_i = qi + wave * D;
     // QK: four lanes per key (lane quad kq = lane / 4 takes key 16 j + kq in
     // sub-pass j), each lane a quarter of the rotation pairs
     constexpr int PPL = H / 4;                    // rotation pairs per lane
@@ -399,6 +406,15 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
         if (bk < 0) continue;
         const int s0 = bk * s.beta + (it % per_blk) * WAVE;
         if (s0 > pos) continue;
+        // the query rotated back by s0 (pair i in lane i): (x c + y s, y c - x s)
+        for (int i = lane; i < H; i += WAVE) {
+            const float x = qr[i], y = qr[i + H];
+            const float c = cos_t[(size_t)s0 * H + i], sn = sin_t[(size_t)s0 * H + i];
+            q_i[i] = x * c + y * sn;
+            q_i[i + H] = y * c - x * sn;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
         // the item's value rows (this lane's dims), issued with the keys so
         // that one wait covers both; rows past pos read row pos (p = 0 there)
         const int klast = pos - s0;
@@ -424,8 +440,9 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
             float acc = 0.0f;
             if (key <= pos) {
                 const size_t ko = base + (size_t)key * rs + part * PPL;
-                const float *cr = cos_t + (size_t)key * H + part * PPL;
-                const float *sr = sin_t + (size_t)key * H + part * PPL;
+                // rotation by the key's offset in the item
+                const float *cr = cos_t + (size_t)(16 * j + kq) * H + part * PPL;
+                const float *sr = sin_t + (size_t)(16 * j + kq) * H + part * PPL;
 #pragma unroll
                 for (int i = 0; i < PPL; i += 4) {
                     float x0[4], x1[4];
@@ -454,8 +471,8 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
                     for (int e = 0; e < 4; ++e) {
                         const float k0 = x0[e] * cc[e] - x1[e] * ss[e];
                         const float k1 = x1[e] * cc[e] + x0[e] * ss[e];
-                        acc = fmaf(qr[i0 + e], k0, acc);
-                        acc = fmaf(qr[i0 + e + H], k1, acc);
+                        acc = fmaf(q_i[i0 + e], k0, acc);
+                        acc = fmaf(q_i[i0 + e + H], k1, acc);
                     }
                 }
             }
