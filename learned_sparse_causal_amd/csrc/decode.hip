@@ -13,37 +13,19 @@
 // whole-sequence build does), and each new query takes the route and the
 // attention that the whole-sequence path gives its position.
 //
-// k_decode_route: one wave per route.  The (batch, kv-head) list offsets and
-//   entries are staged in LDS once.  The rotated query and its code scores go
-//   to LDS (fp32, fused multiply-add chains in dimension order,
-//   rotation products rounded before the add: the same arithmetic as the
-//   whole-sequence router, so the decisions are bit-identical); address sums
-//   are kept per lane.  Addresses are visited in (sum desc, address asc)
-//   order by repeated wave arg-max over the addresses that follow the last
-//   one visited; each visited list contributes its eligible prefix to the
-//   pool until at least n_probes addresses were visited and R blocks pooled.
-//   The pool is reranked by the inner product of the rotated query with the
-//   block summaries and the R best (lower block first on ties) are emitted
-//   in ascending order.
-// k_decode_attend: one workgroup per (batch, q-head).  The local blocks and
-//   the valid, first-occurrence selected blocks are split in 64-key items
-//   over eight waves; four lanes score one key, each wave keeps an online
-//   softmax and accumulates P V with the 64 value rows of an item loaded back
-//   to back, and the eight states are merged through LDS.  Keys are rotated
-//   relative to their item's first position s0: a rotation by s is the
-//   rotation by s0 followed by the one by s - s0, so the score is the query
-//   rotated back by s0 against the key rotated by its offset in the item.
-//   The query's back-rotation is done once per item; the keys then read
-//   only the first 64 rows of the rotary table, which stay in the caches,
-//   instead of one row per key.
+// k_decode_step: one workgroup of eight waves per (batch, q-head).  Wave 0
+//   routes the new query (the lists of its (batch, kv-head) staged in LDS by
+//   the whole workgroup; the arithmetic of the whole-sequence router, so the
+//   decisions are bit-identical) while the other waves attend the local
+//   blocks, which do not depend on the selection; then every wave attends
+//   its share of the selected blocks, in 64-key items with an online
+//   softmax, and the eight states are merged through LDS.
 #include <algorithm>
 #include <climits>
 
 #include "common.hpp"
 
 namespace {
-
-constexpr int DR_THREADS = WAVE;   // one wave per route
 
 // (score, id) as one unsigned 64-bit key: (score, id) is ordered before
 // (score', id') -- score > score', or equal scores and id < id' -- exactly
@@ -90,10 +72,32 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
     return swap_max(k, true);
 }
 
-size_t decode_route_lds(const Shape &s) {
-    // q_rot, code scores, address sums, list offsets, entries, pool ids, pool
-    // scores, extension addresses
-    return (size_t)(s.d + s.P * s.K + s.A + (s.A + 1) + s.NB + 2 * s.NB + std::min(s.A, s.NB)) * 4;
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t k, int src) {
+    const int lo = __shfl((int)(uint32_t)k, src), hi = __shfl((int)(uint32_t)(k >> 32), src);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t k, int m) {
+    const int lo = __shfl_xor((int)(uint32_t)k, m), hi = __shfl_xor((int)(uint32_t)(k >> 32), m);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Bitonic sort of one key per lane, largest first, within aligned groups of
+// SEG lanes (a power of two <= 64).
+template <int SEG>
+__device__ __forceinline__ uint64_t sort_desc(uint64_t k, int lane) {
+    const int i = lane & (SEG - 1);
+#pragma unroll
+    for (int size = 2; size <= SEG; size <<= 1) {
+#pragma unroll
+        for (int j = size >> 1; j > 0; j >>= 1) {
+            const uint64_t o = shfl_xor_u64(k, j);
+            // in a descending run the lower lane of a pair keeps the larger key
+            const bool keep_max = ((i & j) == 0) == ((i & size) == 0);
+            k = keep_max ? key_max(k, o) : (k < o ? k : o);
+        }
+    }
+    return k;
 }
 
 // fp32 fused multiply-add chain over n = N elements in index order, with the
@@ -112,221 +116,24 @@ __device__ __forceinline__ float chain_lds_global(const float *a, const float *_
     return acc;
 }
 
-// Stage n ints from global to LDS, up to SI loads in flight per lane.
-constexpr int SI = 24;
-__device__ __forceinline__ void stage_ints(int *dst, const int32_t *__restrict__ src, int n,
-                                           int lane) {
-    for (int b0 = 0; b0 < n; b0 += SI * WAVE) {
-        int v[SI];
-#pragma unroll
-        for (int k = 0; k < SI; ++k) {
-            const int i = b0 + k * WAVE + lane;
-            v[k] = i < n ? src[i] : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < SI; ++k) {
-            const int i = b0 + k * WAVE + lane;
-            if (i < n) dst[i] = v[k];
-        }
-    }
+constexpr int DS_THREADS = 512;   // one workgroup per route
+constexpr int DS_WAVES = DS_THREADS / WAVE;
+
+// LDS of one workgroup, in 4-byte words.  Attention part: the scaled rotated
+// query [d], per-wave probabilities [W][64], (m, l) [W][2], outputs [W][d],
+// back-rotated queries [W][4][d], blocks [L + R].  Route part: the rotated
+// query [d], code scores [P K], list offsets [A + 1], entries [NB], pool ids
+// [NB], then one area that holds the extension's addresses and their sums
+// ([min(A, NB)] each) and, once the extension is done, the pool's rerank
+// scores [NB].
+size_t decode_attend_words(const Shape &s) {
+    return (size_t)s.d + (size_t)DS_WAVES * (WAVE + 2 + 5 * s.d) + s.L + s.R;
 }
-
-template <int D, int P, bool BF16>
-__global__ __launch_bounds__(DR_THREADS) void k_decode_route(
-    Shape s, int pos, const void *__restrict__ q, const float *__restrict__ cos_t,
-    const float *__restrict__ sin_t, const float *__restrict__ cb, const float *__restrict__ kbar,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ entries,
-    int32_t *__restrict__ sel) {
-    constexpr int H = D / 2, DS = D / P;
-    extern __shared__ __align__(16) float dr_lds[];
-    const int R = s.R, K = s.K, A = s.A, NB = s.NB;
-    float *qr = dr_lds;                                  // [D] rotated query
-    float *sc = qr + D;                                  // [P K] code scores
-    float *sig = sc + P * K;                             // [A] address sums
-    int *off = reinterpret_cast<int *>(sig + A);         // [A + 1] list offsets
-    int *ent = off + A + 1;                              // [NB] list entries
-    int *pool_n = ent + NB;                              // [NB] pooled blocks
-    float *pool_r = reinterpret_cast<float *>(pool_n + NB);   // [NB] their rerank scores
-    int *cand = reinterpret_cast<int *>(pool_r + NB);    // [min(A, NB)] extension addresses
-
-    const int route = blockIdx.x;                        // b * Hq + h
-    const int b = route / s.Hq, h = route % s.Hq, g = h / s.G;
-    const int lane = threadIdx.x;
-    const uint64_t lanemask = (1ull << lane) - 1ull;
-    int32_t *out = sel + (size_t)route * R;
-    const int qb = pos / s.beta;
-    const int E = max(0, qb - s.L + 1);
-    if (E <= R) {   // bypass: every eligible block, in order
-        for (int r = lane; r < R; r += WAVE) out[r] = r < E ? r : -1;
-        return;
-    }
-    const size_t u = (size_t)b * s.Hkv + g;
-    // Every load that does not depend on another goes out first: this lane's
-    // query pair(s) and rotary values, its codebook row(s) (codes lane and
-    // lane + 64), then the (batch, kv-head) lists staged into LDS.
-    const size_t qoff = (size_t)route * D;
-    constexpr int QP = (H + WAVE - 1) / WAVE;            // query pairs per lane
-    float qa[QP], qb2[QP], qc[QP], qs[QP];
-#pragma unroll
-    for (int k = 0; k < QP; ++k) {
-        const int i = lane + k * WAVE;
-        const bool ok = i < H;
-        qa[k] = ok ? load1<BF16>(q, qoff + i) : 0.0f;
-        qb2[k] = ok ? load1<BF16>(q, qoff + i + H) : 0.0f;
-        qc[k] = ok ? cos_t[(size_t)pos * H + i] : 0.0f;
-        qs[k] = ok ? sin_t[(size_t)pos * H + i] : 0.0f;
-    }
-    float4 crow[2][DS / 4];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int x = lane + k * WAVE;
-        const int xc = x < P * K ? x : 0;                 // in bounds; unused past P K
-        const float4 *cr = reinterpret_cast<const float4 *>(
-            cb + (((size_t)g * P + xc / K) * K + xc % K) * DS);
-        if (k == 0 || (P == 2 && P * K > WAVE)) {
-#pragma unroll
-            for (int j = 0; j < DS / 4; ++j) crow[k][j] = cr[j];
-        }
-    }
-    stage_ints(off, offsets + u * (A + 1), A + 1, lane);
-    stage_ints(ent, entries + u * NB, NB, lane);
-    // rotate (fp32, products rounded before the add)
-#pragma unroll
-    for (int k = 0; k < QP; ++k) {
-        const int i = lane + k * WAVE;
-        if (i < H) {
-            const float ac = qa[k] * qc[k], bs = qb2[k] * qs[k];
-            const float bc = qb2[k] * qc[k], as = qa[k] * qs[k];
-            qr[i] = ac - bs;
-            qr[i + H] = bc + as;
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    // code scores: fma chains in dimension order
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int x = lane + k * WAVE;
-        if ((k == 0 || (P == 2 && P * K > WAVE)) && x < P * K) {
-            const float *qp = qr + (x / K) * DS;
-            float acc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < DS / 4; ++j) {
-                acc = fmaf(qp[4 * j], crow[k][j].x, acc);
-                acc = fmaf(qp[4 * j + 1], crow[k][j].y, acc);
-                acc = fmaf(qp[4 * j + 2], crow[k][j].z, acc);
-                acc = fmaf(qp[4 * j + 3], crow[k][j].w, acc);
-            }
-            sc[x] = acc;
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    // address sums, component 0 first (mixed radix, component 0 most significant)
-    for (int a = lane; a < A; a += WAVE) sig[a] = P == 1 ? sc[a] : sc[a / K] + sc[K + a % K];
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-
-    const int last = qb - s.L;
-    int npool = 0;
-    // the eligible prefix of list a joins the pool
-    auto take = [&](int a) {
-        const int e0 = off[a], e1 = off[a + 1];
-        for (int e = e0; e < e1; e += WAVE) {
-            const int n = e + lane < e1 ? ent[e + lane] : INT_MAX;
-            const bool ok = n <= last;
-            const uint64_t m = __ballot(ok);
-            const int slot = npool + __popcll(m & lanemask);
-            if (ok && slot < NB) pool_n[slot] = n;   // a valid index holds <= NB blocks
-            npool = min(NB, npool + __popcll(m));
-            if (m != ~0ull) break;   // a later block ends the prefix
-        }
-    };
-    // The walk over addresses in (sum desc, address asc) order stops at the
-    // first address at which at least n_probes were visited and R blocks
-    // pooled.  Phase 1 visits the n_probes best addresses; after them only
-    // addresses whose list has an eligible block can change the pool or end
-    // the walk, so phase 2 walks those alone (at most R more rounds).
-    uint64_t prev = ~0ull;                               // key of the last visited address
-    const int np1 = min(A, s.npr);
-    for (int r = 0; r < np1; ++r) {
-        uint64_t best = 0;
-        for (int a = lane; a < A; a += WAVE) {
-            const uint64_t k = order_key(sig[a], a);
-            if (k < prev) best = key_max(best, k);
-        }
-        best = wave_max_key(best);
-        prev = best;
-        take(key_id(best));
-    }
-    if (npool < R && np1 < A) {
-        // addresses after the last visited one whose list starts with an eligible block
-        int ncand = 0;
-        for (int a0 = 0; a0 < A; a0 += WAVE) {
-            const int a = a0 + lane;
-            bool ok = false;
-            if (a < A) {
-                const int e0 = off[a];
-                ok = e0 < off[a + 1] && ent[e0] <= last && order_key(sig[a], a) < prev;
-            }
-            const uint64_t m = __ballot(ok);
-            if (ok) cand[ncand + __popcll(m & lanemask)] = a;
-            ncand += __popcll(m);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        while (npool < R) {
-            uint64_t best = 0;
-            for (int x = lane; x < ncand; x += WAVE) {
-                const int a = cand[x];
-                const uint64_t k = order_key(sig[a], a);
-                if (k < prev) best = key_max(best, k);
-            }
-            best = wave_max_key(best);
-            if (best == 0) break;                        // every list taken
-            prev = best;
-            take(key_id(best));
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    // rerank: fma chain over every dimension of q_rot . kbar_n
-    const float *kb = kbar + u * (size_t)NB * D;
-    for (int x = lane; x < npool; x += WAVE)
-        pool_r[x] = chain_lds_global<D>(qr, kb + (size_t)pool_n[x] * D);
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    // the R best in (score desc, block asc) order; lane r keeps pick r
-    // (R <= 16 whenever the search runs)
-    const int nsel = min(R, npool);
-    uint64_t pprev = ~0ull;
-    int mine = -1;
-    for (int r = 0; r < nsel; ++r) {
-        uint64_t best = 0;
-        for (int x = lane; x < npool; x += WAVE) {
-            const uint64_t k = order_key(pool_r[x], pool_n[x]);
-            if (k < pprev) best = key_max(best, k);
-        }
-        best = wave_max_key(best);
-        pprev = best;
-        if (r == lane) mine = key_id(best);
-    }
-    // ascending: a pick's slot is the number of smaller picks
-    int rank = 0;
-    for (int r = 0; r < nsel; ++r) {
-        const int other = __shfl(mine, r);
-        rank += other < mine ? 1 : 0;
-    }
-    if (lane < nsel) out[rank] = mine;
-    for (int r = nsel + lane; r < R; r += WAVE) out[r] = -1;
+size_t decode_route_words(const Shape &s) {
+    const size_t ac = (size_t)std::min(s.A, s.NB);
+    return (size_t)s.d + s.P * s.K + (s.A + 1) + 2 * (size_t)s.NB + std::max(2 * ac, (size_t)s.NB);
 }
-
-constexpr int DA_THREADS = 512;
-constexpr int DA_WAVES = DA_THREADS / WAVE;
-
-size_t decode_attend_lds(const Shape &s) {
-    return (size_t)(s.d + DA_WAVES * (WAVE + 2 + 2 * s.d)) * 4 + (size_t)(s.R + s.L) * 4;
-}
+size_t decode_step_lds(const Shape &s) { return (decode_attend_words(s) + decode_route_words(s)) * 4; }
 
 // DPL consecutive elements starting at i, as floats.
 template <bool BF16, int DPL>
@@ -345,50 +152,125 @@ __device__ __forceinline__ void load_run(const void *base, size_t i, float (&x)[
     }
 }
 
-// One workgroup per (batch, q-head), 8 waves.  Logits in base 2: q is
-// pre-scaled by log2(e)/sqrt(d).  Lane l owns output dims DPL l .. DPL l + DPL-1.
-template <int D, bool BF16>
-__global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
+// One workgroup of eight waves per (batch, q-head) route.
+//  - Every thread: the rotated query (unscaled for the route, pre-scaled by
+//    log2(e)/sqrt(d) for the attention), the (batch, kv-head) list offsets
+//    and entries staged in LDS, and the local blocks.
+//  - Wave 0 routes (below) while waves 1..7 attend the local blocks, which
+//    do not depend on the selection.
+//  - After a barrier every wave attends its share of the selected blocks,
+//    and the eight online-softmax states are merged through LDS.
+// Route (wave 0): code scores are fp32 fused multiply-add chains in dimension
+// order, the rotation products rounded before the add: the arithmetic of the
+// whole-sequence router, so the decisions are bit-identical.  Addresses are
+// visited in (sum desc, address asc) order by repeated wave arg-max over the
+// addresses that follow the last one visited; each visited list contributes
+// its eligible prefix to the pool until at least n_probes addresses were
+// visited and R blocks pooled.  The pool is reranked by the inner product of
+// the rotated query with the block summaries and the R best (lower block
+// first on ties) are kept in ascending order.
+// Attention: the blocks are split in 64-key items; four lanes score one key,
+// each wave keeps an online softmax and accumulates P V with the 64 value
+// rows of an item loaded back to back.  Keys are rotated relative to their
+// item's first position s0 (a rotation by s is the one by s0 followed by the
+// one by s - s0): the query rotated back by s0 meets the key rotated by its
+// offset in the item, so the keys read only the first 64 rotary rows.
+template <int D, int P, bool BF16>
+__global__ __launch_bounds__(DS_THREADS) void k_decode_step(
     Shape s, int pos, const void *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, const float *__restrict__ cos_t, const float *__restrict__ sin_t,
-    const int32_t *__restrict__ sel, void *__restrict__ out) {
-    constexpr int H = D / 2;
+    const float *__restrict__ cb, const float *__restrict__ kbar,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ entries,
+    int32_t *__restrict__ sel, void *__restrict__ out) {
+    constexpr int H = D / 2, DS = D / P;
     constexpr int DPL = D / WAVE;                 // output dims per lane
-    extern __shared__ __align__(16) float da_lds[];
-    float *qr = da_lds;                           // [D]
-    float *pw = qr + D;                           // [DA_WAVES][WAVE] probabilities
-    float *ml = pw + DA_WAVES * WAVE;             // [DA_WAVES][2] (m, l)
-    float *ow = ml + DA_WAVES * 2;                // [DA_WAVES][D]
-    float *qi = ow + DA_WAVES * D;                // [DA_WAVES][D] query rotated back by s0
-    int *blk = reinterpret_cast<int *>(qi + DA_WAVES * D);   // [L + R]
+    extern __shared__ __align__(16) float dstep_lds[];
+    const int R = s.R, K = s.K, A = s.A, NB = s.NB;
+    // attention part
+    float *qa = dstep_lds;                        // [D] scaled rotated query
+    float *pw = qa + D;                           // [W][64] probabilities
+    float *ml = pw + DS_WAVES * WAVE;             // [W][2] (m, l)
+    float *ow = ml + DS_WAVES * 2;                // [W][D]
+    float *qi = ow + DS_WAVES * D;                // [W][4][D] query rotated back by s0 + 16 j
+    int *blk = reinterpret_cast<int *>(qi + DS_WAVES * 4 * D);   // [L + R]
+    // route part
+    float *qr = reinterpret_cast<float *>(blk + s.L + R);    // [D] rotated query
+    float *sc = qr + D;                                  // [P K] code scores
+    int *off = reinterpret_cast<int *>(sc + P * K);      // [A + 1] list offsets
+    int *ent = off + A + 1;                              // [NB] list entries
+    int *pool_n = ent + NB;                              // [NB] pooled blocks
+    float *un = reinterpret_cast<float *>(pool_n + NB);
+    const int AC = min(A, NB);
+    int *cand = reinterpret_cast<int *>(un);             // [AC] extension addresses
+    float *sig = un + AC;                                // [AC] their sums
+    float *pool_r = un;                                  // [NB] rerank scores (after the extension)
 
-    const int route = blockIdx.x;
+    const int route = blockIdx.x;                        // b * Hq + h
     const int b = route / s.Hq, h = route % s.Hq, g = h / s.G;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-    const int qb = pos / s.beta, R = s.R;
+    const uint64_t lanemask = (1ull << lane) - 1ull;
+    int32_t *out_sel = sel + (size_t)route * R;
+    const int qb = pos / s.beta;
+    const int E = max(0, qb - s.L + 1);
+    const bool search = E > R;
+    const size_t u = (size_t)b * s.Hkv + g;
+    const size_t qoff = (size_t)route * D;
     const int lo = max(0, qb - s.L + 1);
     const int nloc = qb - lo + 1;
+    const int per_blk = s.beta / WAVE;
+    const int nloc_items = nloc * per_blk;
+    const int nitems = (nloc + R) * per_blk;
+
+    // wave 0's codebook rows (codes lane and lane + 64), in flight during
+    // the set-up below
+    float4 crow[2][DS / 4];
+    if (wave == 0 && search) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int x = lane + k * WAVE;
+            const int xc = x < P * K ? x : 0;             // in bounds; unused past P K
+            const float4 *cr = reinterpret_cast<const float4 *>(
+                cb + (((size_t)g * P + xc / K) * K + xc % K) * DS);
+            if (k == 0 || (P == 2 && P * K > WAVE)) {
+#pragma unroll
+                for (int j = 0; j < DS / 4; ++j) crow[k][j] = cr[j];
+            }
+        }
+    }
+    // rotated query (fp32, products rounded before the add)
     const float scale = 1.4426950408889634f / sqrtf((float)D);
-    const size_t qoff = (size_t)route * D;
-    for (int i = tid; i < H; i += DA_THREADS) {
+    for (int i = tid; i < H; i += DS_THREADS) {
         const float a = load1<BF16>(q, qoff + i), bb = load1<BF16>(q, qoff + i + H);
         const float c = cos_t[(size_t)pos * H + i], sn = sin_t[(size_t)pos * H + i];
-        qr[i] = (a * c - bb * sn) * scale;
-        qr[i + H] = (bb * c + a * sn) * scale;
+        const float ac = a * c, bs = bb * sn, bc = bb * c, as = a * sn;
+        const float r0 = ac - bs, r1 = bc + as;
+        qr[i] = r0;
+        qr[i + H] = r1;
+        qa[i] = r0 * scale;
+        qa[i + H] = r1 * scale;
     }
-    // blocks: the local ones, then the valid first occurrences of the selection
-    const int32_t *row = sel + (size_t)route * R;
-    for (int j = tid; j < nloc; j += DA_THREADS) blk[j] = lo + j;
-    for (int r = tid; r < R; r += DA_THREADS) {
-        const int id = row[r];
-        bool ok = id >= 0 && id <= qb - s.L;
-        for (int r2 = 0; ok && r2 < r; ++r2) ok = row[r2] != id;
-        blk[nloc + r] = ok ? id : -1;
+    // list offsets and entries, four loads in flight per thread
+    if (search) {
+        const int32_t *og = offsets + u * (A + 1), *eg = entries + u * NB;
+        const int n_off = A + 1, n_all = A + 1 + NB;
+        for (int b0 = 0; b0 < n_all; b0 += 4 * DS_THREADS) {
+            int v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = min(b0 + k * DS_THREADS + tid, n_all - 1);
+                v[k] = i < n_off ? og[i] : eg[i - n_off];
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int i = b0 + k * DS_THREADS + tid;
+                if (i < n_all) off[i] = v[k];   // ent follows off in LDS
+            }
+        }
     }
+    for (int j = tid; j < nloc; j += DS_THREADS) blk[j] = lo + j;
     __syncthreads();
 
-    const int per_blk = s.beta / WAVE;
-    const int nitems = (nloc + R) * per_blk;
+    // ---- attention state of this wave, and one 64-key item
     float m = -INFINITY, l = 0.0f;
     float o[DPL];
 #pragma unroll
@@ -396,27 +278,61 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
     const size_t rs = (size_t)s.Hkv * D;          // cache row stride (elements)
     const size_t base = ((size_t)b * s.T * s.Hkv + g) * D;
     float *p_s = pw + wave * WAVE;
-    float *q_i = qi + wave * D;
-    // QK: four lanes per key (lane quad kq = lane / 4 takes key 16 j + kq in
-    // sub-pass j), each lane a quarter of the rotation pairs
+    float *q_i = qi + wave * 4 * D;
+    // QK: four lanes per key (lane quad kq = lane / 4 takes key 16 j + kq of
+    // an item in sub-pass j), each lane a quarter of the rotation pairs.  The
+    // key at s0 + 16 j + kq is rotated by kq here (the lane's rotary rows,
+    // loaded once) and the query back by s0 + 16 j.
     constexpr int PPL = H / 4;                    // rotation pairs per lane
+    constexpr int NI = PPL / 4;                   // their groups of four
     const int part = lane & 3, kq = lane >> 2;
-    for (int it = wave; it < nitems; it += DA_WAVES) {
+    // back-rotation of the query: lane takes sub-pass jq = lane / 16 and
+    // pairs QPL (lane % 16) .. QPL (lane % 16) + QPL - 1
+    constexpr int QPL = H / 16;
+    const int jq = lane >> 4, pq = (lane & 15) * QPL;
+    // bf16: every sub-pass's key words are loaded before the values
+    constexpr int KJ = BF16 ? 4 : 1;
+    auto attend_item = [&](int it) {
         const int bk = blk[it / per_blk];
-        if (bk < 0) continue;
+        if (bk < 0) return;
         const int s0 = bk * s.beta + (it % per_blk) * WAVE;
-        if (s0 > pos) continue;
-        // the query rotated back by s0 (pair i in lane i): (x c + y s, y c - x s)
-        for (int i = lane; i < H; i += WAVE) {
-            const float x = qr[i], y = qr[i + H];
-            const float c = cos_t[(size_t)s0 * H + i], sn = sin_t[(size_t)s0 * H + i];
-            q_i[i] = x * c + y * sn;
-            q_i[i + H] = y * c - x * sn;
+        if (s0 > pos) return;
+        // loads in the order they are waited for: the rotary rows (the
+        // lane's keys' offsets kq, the query's s0 + 16 jq), the keys, then
+        // the values
+        float rc[PPL], rsn[PPL];
+#pragma unroll
+        for (int n = 0; n < NI; ++n) {
+            const float4 c4 = *reinterpret_cast<const float4 *>(cos_t + (size_t)kq * H + part * PPL + 4 * n);
+            const float4 s4 = *reinterpret_cast<const float4 *>(sin_t + (size_t)kq * H + part * PPL + 4 * n);
+            rc[4 * n] = c4.x; rc[4 * n + 1] = c4.y; rc[4 * n + 2] = c4.z; rc[4 * n + 3] = c4.w;
+            rsn[4 * n] = s4.x; rsn[4 * n + 1] = s4.y; rsn[4 * n + 2] = s4.z; rsn[4 * n + 3] = s4.w;
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        // the item's value rows (this lane's dims), issued with the keys so
-        // that one wait covers both; rows past pos read row pos (p = 0 there)
+        float cq[QPL], sq[QPL];
+        {
+            const size_t row = (size_t)min(s0 + 16 * jq, s.T - 1) * H + pq;   // unused past pos
+#pragma unroll
+            for (int e = 0; e < QPL; ++e) {
+                cq[e] = cos_t[row + e];
+                sq[e] = sin_t[row + e];
+            }
+        }
+        // key row of sub-pass j for this lane (keys past pos read row pos)
+        auto krow = [&](int j) { return base + (size_t)min(s0 + 16 * j + kq, pos) * rs + part * PPL; };
+        uint2 ku0[KJ][NI], ku1[KJ][NI];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u16 *kr = reinterpret_cast<const u16 *>(kc) + krow(j);
+#pragma unroll
+                for (int n = 0; n < NI; ++n) {
+                    ku0[j][n] = *reinterpret_cast<const uint2 *>(kr + 4 * n);
+                    ku1[j][n] = *reinterpret_cast<const uint2 *>(kr + 4 * n + H);
+                }
+            }
+        }
+        // the item's value rows (this lane's dims); rows past pos read row
+        // pos (p = 0 there)
         const int klast = pos - s0;
         constexpr int RW = BF16 ? 1 : DPL;        // 32-bit words of raw values per key
         uint32_t vr[WAVE][RW];
@@ -433,47 +349,44 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
                     vr[kk][j] = __float_as_uint(reinterpret_cast<const float *>(vc)[vo + j]);
             }
         }
+        // the query rotated back by s0 + 16 jq: (x c + y s, y c - x s)
+#pragma unroll
+        for (int e = 0; e < QPL; ++e) {
+            const float x = qa[pq + e], y = qa[pq + e + H];
+            q_i[jq * D + pq + e] = x * cq[e] + y * sq[e];
+            q_i[jq * D + pq + e + H] = y * cq[e] - x * sq[e];
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): q_i written
+        __builtin_amdgcn_wave_barrier();
         float lg[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = s0 + 16 * j + kq;
+            const float *qj = q_i + j * D + part * PPL;
             float acc = 0.0f;
-            if (key <= pos) {
-                const size_t ko = base + (size_t)key * rs + part * PPL;
-                // rotation by the key's offset in the item
-                const float *cr = cos_t + (size_t)(16 * j + kq) * H + part * PPL;
-                const float *sr = sin_t + (size_t)(16 * j + kq) * H + part * PPL;
 #pragma unroll
-                for (int i = 0; i < PPL; i += 4) {
-                    float x0[4], x1[4];
-                    if constexpr (BF16) {
-                        const uint2 u0 = *reinterpret_cast<const uint2 *>(
-                            reinterpret_cast<const u16 *>(kc) + ko + i);
-                        const uint2 u1 = *reinterpret_cast<const uint2 *>(
-                            reinterpret_cast<const u16 *>(kc) + ko + i + H);
-                        x0[0] = __uint_as_float(u0.x << 16); x0[1] = __uint_as_float(u0.x & 0xFFFF0000u);
-                        x0[2] = __uint_as_float(u0.y << 16); x0[3] = __uint_as_float(u0.y & 0xFFFF0000u);
-                        x1[0] = __uint_as_float(u1.x << 16); x1[1] = __uint_as_float(u1.x & 0xFFFF0000u);
-                        x1[2] = __uint_as_float(u1.y << 16); x1[3] = __uint_as_float(u1.y & 0xFFFF0000u);
-                    } else {
-                        const float4 f0 = *reinterpret_cast<const float4 *>(
-                            reinterpret_cast<const float *>(kc) + ko + i);
-                        const float4 f1 = *reinterpret_cast<const float4 *>(
-                            reinterpret_cast<const float *>(kc) + ko + i + H);
-                        x0[0] = f0.x; x0[1] = f0.y; x0[2] = f0.z; x0[3] = f0.w;
-                        x1[0] = f1.x; x1[1] = f1.y; x1[2] = f1.z; x1[3] = f1.w;
-                    }
-                    const float4 c4 = *reinterpret_cast<const float4 *>(cr + i);
-                    const float4 s4 = *reinterpret_cast<const float4 *>(sr + i);
-                    const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
-                    const int i0 = part * PPL + i;
+            for (int n = 0; n < NI; ++n) {
+                float x0[4], x1[4];
+                if constexpr (BF16) {
+                    const uint2 u0 = ku0[j][n], u1 = ku1[j][n];
+                    x0[0] = __uint_as_float(u0.x << 16); x0[1] = __uint_as_float(u0.x & 0xFFFF0000u);
+                    x0[2] = __uint_as_float(u0.y << 16); x0[3] = __uint_as_float(u0.y & 0xFFFF0000u);
+                    x1[0] = __uint_as_float(u1.x << 16); x1[1] = __uint_as_float(u1.x & 0xFFFF0000u);
+                    x1[2] = __uint_as_float(u1.y << 16); x1[3] = __uint_as_float(u1.y & 0xFFFF0000u);
+                } else {
+                    const float *kr = reinterpret_cast<const float *>(kc) + krow(j);
+                    const float4 f0 = *reinterpret_cast<const float4 *>(kr + 4 * n);
+                    const float4 f1 = *reinterpret_cast<const float4 *>(kr + 4 * n + H);
+                    x0[0] = f0.x; x0[1] = f0.y; x0[2] = f0.z; x0[3] = f0.w;
+                    x1[0] = f1.x; x1[1] = f1.y; x1[2] = f1.z; x1[3] = f1.w;
+                }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float k0 = x0[e] * cc[e] - x1[e] * ss[e];
-                        const float k1 = x1[e] * cc[e] + x0[e] * ss[e];
-                        acc = fmaf(q_i[i0 + e], k0, acc);
-                        acc = fmaf(q_i[i0 + e + H], k1, acc);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const float cc = rc[4 * n + e], ss = rsn[4 * n + e];
+                    const float k0 = x0[e] * cc - x1[e] * ss;
+                    const float k1 = x1[e] * cc + x0[e] * ss;
+                    acc = fmaf(qj[4 * n + e], k0, acc);
+                    acc = fmaf(qj[4 * n + e + H], k1, acc);
                 }
             }
             // sum over the lane quad
@@ -518,7 +431,219 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
             for (int j = 0; j < DPL; ++j) o[j] = fmaf(pk, x[j], o[j]);
         }
         __builtin_amdgcn_wave_barrier();
+    };
+
+    int *blk_rem = blk + nloc;                    // [R] the selection, for the attention
+    if (wave == 0) {
+        if (!search) {   // bypass: every eligible block, in order
+            for (int r = lane; r < R; r += WAVE) {
+                const int id = r < E ? r : -1;
+                out_sel[r] = id;
+                blk_rem[r] = id;
+            }
+        } else {
+            // code scores: fma chains in dimension order
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int x = lane + k * WAVE;
+                if ((k == 0 || (P == 2 && P * K > WAVE)) && x < P * K) {
+                    const float *qp = qr + (x / K) * DS;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < DS / 4; ++j) {
+                        acc = fmaf(qp[4 * j], crow[k][j].x, acc);
+                        acc = fmaf(qp[4 * j + 1], crow[k][j].y, acc);
+                        acc = fmaf(qp[4 * j + 2], crow[k][j].z, acc);
+                        acc = fmaf(qp[4 * j + 3], crow[k][j].w, acc);
+                    }
+                    sc[x] = acc;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            const int last = qb - s.L;
+            int npool = 0;
+            // the eligible prefix of list a joins the pool
+            auto take = [&](int a) {
+                const int e0 = off[a], e1 = off[a + 1];
+                for (int e = e0; e < e1; e += WAVE) {
+                    const int n = e + lane < e1 ? ent[e + lane] : INT_MAX;
+                    const bool ok = n <= last;
+                    const uint64_t msk = __ballot(ok);
+                    const int slot = npool + __popcll(msk & lanemask);
+                    if (ok && slot < NB) pool_n[slot] = n;   // a valid index holds <= NB blocks
+                    npool = min(NB, npool + __popcll(msk));
+                    if (msk != ~0ull) break;   // a later block ends the prefix
+                }
+            };
+            // address sum, component 0 first (mixed radix, component 0 most significant)
+            auto sigma = [&](int c0, int c1) { return P == 1 ? sc[c0] : sc[c0] + sc[K + c1]; };
+            // The walk over addresses in (sum desc, address asc) order stops at
+            // the first address at which at least n_probes were visited and R
+            // blocks pooled.  Phase 1 visits the n_probes best addresses.  An
+            // address of codes ranked x and y in their components (score desc,
+            // code asc) has (x+1)(y+1)-1 addresses before it in walk order, so
+            // the n_probes best are among the pairs with (x+1)(y+1) <= n_probes
+            // (at most 50 for 16 probes): the codes of each component are
+            // sorted (one wave sort), then those pairs, and the first n_probes
+            // are the walk's.
+            const int np1 = min(A, s.npr);
+            uint64_t wk;                             // lane r: key of the r-th visited address
+            if constexpr (P == 1) {
+                wk = sort_desc<64>(lane < K ? order_key(sc[lane], lane) : 0ull, lane);
+            } else {
+                uint64_t k0, k1;                     // sorted codes of components 0 and 1
+                if (K <= 32) {
+                    const int c = lane & 31, p = lane >> 5;
+                    const uint64_t ks = sort_desc<32>(c < K ? order_key(sc[p * K + c], c) : 0ull, lane);
+                    k0 = ks;                         // lanes 0..31: component 0
+                    k1 = shfl_xor_u64(ks, 32);       // lanes 0..31: component 1
+                } else {
+                    k0 = sort_desc<64>(lane < K ? order_key(sc[lane], lane) : 0ull, lane);
+                    k1 = sort_desc<64>(lane < K ? order_key(sc[K + lane], lane) : 0ull, lane);
+                }
+                // lane -> its pair (x, y), x-major
+                int rem = lane, px = -1, py = 0;
+                for (int x = 0; x < min(s.npr, K); ++x) {
+                    const int cnt = min(s.npr / (x + 1), K);
+                    if (px < 0) {
+                        if (rem < cnt) { px = x; py = rem; }
+                        else rem -= cnt;
+                    }
+                }
+                const uint64_t kx = shfl_u64(k0, max(px, 0)), ky = shfl_u64(k1, py);
+                const int c0 = key_id(kx), c1 = key_id(ky);
+                const bool ok = px >= 0 && kx != 0ull && ky != 0ull;
+                wk = sort_desc<64>(ok ? order_key(sigma(c0, c1), c0 * K + c1) : 0ull, lane);
+            }
+            for (int r = 0; r < np1; ++r) take(key_id(shfl_u64(wk, r)));
+            const uint64_t prev = shfl_u64(wk, np1 - 1);   // key of the last visited address
+            const int npool1 = npool;
+            const float *kb = kbar + u * (size_t)NB * D;
+            // the summary rows of the first 64 pooled blocks, in flight during
+            // the extension (lanes without a block read row 0)
+            constexpr bool PREFETCH = BF16 || D == 64;
+            constexpr int KPW = PREFETCH ? D / 4 : 1;
+            float4 kpre[KPW];
+            if constexpr (PREFETCH) {
+                const float4 *kr = reinterpret_cast<const float4 *>(
+                    kb + (size_t)(lane < npool1 ? pool_n[lane] : 0) * D);
+#pragma unroll
+                for (int j = 0; j < KPW; ++j) kpre[j] = kr[j];
+            }
+            // Phase 2: after the n_probes best only addresses whose list has an
+            // eligible block can change the pool or end the walk; they are
+            // walked alone (at most R more rounds, each by a wave arg-max over
+            // them; candidate x holds its address in cand[x] and its sum in
+            // sig[x]).
+            if (npool < R && np1 < A) {
+                int ncand = 0;
+                // lane's address a0 + lane as codes (c0, c1), advanced by 64 per step
+                int c0 = P == 1 ? lane : lane / K, c1 = P == 1 ? 0 : lane % K;
+                const int s0 = P == 1 ? WAVE : WAVE / K, s1 = P == 1 ? 0 : WAVE % K;
+                for (int a0 = 0; a0 < A; a0 += WAVE) {
+                    const int a = a0 + lane;
+                    bool ok = false;
+                    float sg = 0.0f;
+                    if (a < A) {
+                        const int e0 = off[a];
+                        if (e0 < off[a + 1] && ent[e0] <= last) {
+                            sg = sigma(c0, c1);
+                            ok = order_key(sg, a) < prev;
+                        }
+                    }
+                    const uint64_t msk = __ballot(ok);
+                    if (ok) {
+                        const int x = ncand + __popcll(msk & lanemask);
+                        cand[x] = a;
+                        sig[x] = sg;
+                    }
+                    ncand += __popcll(msk);
+                    c0 += s0;
+                    c1 += s1;
+                    if (P == 2 && c1 >= K) { c1 -= K; ++c0; }
+                }
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                __builtin_amdgcn_wave_barrier();
+                uint64_t pv = prev;
+                while (npool < R) {
+                    uint64_t best = 0;
+                    for (int x = lane; x < ncand; x += WAVE) {
+                        const uint64_t k = order_key(sig[x], cand[x]);
+                        if (k < pv) best = key_max(best, k);
+                    }
+                    best = wave_max_key(best);
+                    if (best == 0) break;                    // every list taken
+                    pv = best;
+                    take(key_id(best));
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            // rerank: fma chain over every dimension of q_rot . kbar_n
+            for (int x = lane; x < npool; x += WAVE) {
+                float acc;
+                if (PREFETCH && x == lane && lane < npool1) {
+                    acc = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < KPW; ++j) {
+                        acc = fmaf(qr[4 * j], kpre[j].x, acc);
+                        acc = fmaf(qr[4 * j + 1], kpre[j].y, acc);
+                        acc = fmaf(qr[4 * j + 2], kpre[j].z, acc);
+                        acc = fmaf(qr[4 * j + 3], kpre[j].w, acc);
+                    }
+                } else {
+                    acc = chain_lds_global<D>(qr, kb + (size_t)pool_n[x] * D);
+                }
+                pool_r[x] = acc;
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            // the R best in (score desc, block asc) order; lane r keeps pick r
+            // (R <= 16 whenever the search runs): one wave sort when the pool
+            // fits the wave, else R rounds of arg-max
+            const int nsel = min(R, npool);
+            int mine = -1;
+            if (npool <= WAVE) {
+                const uint64_t k = sort_desc<64>(
+                    lane < npool ? order_key(pool_r[lane], pool_n[lane]) : 0ull, lane);
+                if (lane < nsel) mine = key_id(k);
+            } else {
+                uint64_t pprev = ~0ull;
+                for (int r = 0; r < nsel; ++r) {
+                    uint64_t best = 0;
+                    for (int x = lane; x < npool; x += WAVE) {
+                        const uint64_t k = order_key(pool_r[x], pool_n[x]);
+                        if (k < pprev) best = key_max(best, k);
+                    }
+                    best = wave_max_key(best);
+                    pprev = best;
+                    if (r == lane) mine = key_id(best);
+                }
+            }
+            // ascending: a pick's slot is the number of smaller picks
+            int rank = 0;
+            for (int r = 0; r < nsel; ++r) {
+                const int other = __shfl(mine, r);
+                rank += other < mine ? 1 : 0;
+            }
+            if (lane < nsel) {
+                out_sel[rank] = mine;
+                blk_rem[rank] = mine;   // distinct and eligible: pooled blocks are
+            }
+            for (int r = nsel + lane; r < R; r += WAVE) {
+                out_sel[r] = -1;
+                blk_rem[r] = -1;
+            }
+        }
+    } else {
+        // the local blocks, while wave 0 routes
+        for (int it = wave - 1; it < nloc_items; it += DS_WAVES - 1) attend_item(it);
     }
+    __syncthreads();
+    // the selected blocks, on every wave
+    for (int it = nloc_items + wave; it < nitems; it += DS_WAVES) attend_item(it);
+
     // merge the waves' states
     if (lane == 0) {
         ml[2 * wave] = m;
@@ -529,11 +654,11 @@ __global__ __launch_bounds__(DA_THREADS) void k_decode_attend(
     __syncthreads();
     if (wave == 0) {
         float M = -INFINITY;
-        for (int w = 0; w < DA_WAVES; ++w) M = fmaxf(M, ml[2 * w]);
+        for (int w = 0; w < DS_WAVES; ++w) M = fmaxf(M, ml[2 * w]);
         float lt = 0.0f, acc[DPL];
 #pragma unroll
         for (int j = 0; j < DPL; ++j) acc[j] = 0.0f;
-        for (int w = 0; w < DA_WAVES; ++w) {
+        for (int w = 0; w < DS_WAVES; ++w) {
             const float mw = ml[2 * w];
             if (mw == -INFINITY) continue;        // a wave with no item
             const float f = __builtin_amdgcn_exp2f(mw - M);
@@ -558,26 +683,12 @@ hipError_t run_decode(const Shape &s, int pos, const void *q, const void *kc, co
                       const int32_t *offsets, const int32_t *entries, int32_t *sel, void *out,
                       hipStream_t st) {
     const unsigned routes = (unsigned)(s.B * s.Hq);
-    const size_t lr = decode_route_lds(s);
-    hipError_t e;
-    if (s.P == 1) {
-        e = lds_at_least(k_decode_route<D, 1, BF16>, lr);
-        if (e != hipSuccess) return e;
-        k_decode_route<D, 1, BF16><<<routes, DR_THREADS, lr, st>>>(s, pos, q, cos_t, sin_t, cb,
-                                                                   kbar, offsets, entries, sel);
-    } else {
-        e = lds_at_least(k_decode_route<D, 2, BF16>, lr);
-        if (e != hipSuccess) return e;
-        k_decode_route<D, 2, BF16><<<routes, DR_THREADS, lr, st>>>(s, pos, q, cos_t, sin_t, cb,
-                                                                   kbar, offsets, entries, sel);
-    }
-    e = hipGetLastError();
+    const size_t lds = decode_step_lds(s);
+    auto *fn = s.P == 1 ? k_decode_step<D, 1, BF16> : k_decode_step<D, 2, BF16>;
+    const hipError_t e = lds_at_least(fn, lds);
     if (e != hipSuccess) return e;
-    const size_t la = decode_attend_lds(s);
-    e = lds_at_least(k_decode_attend<D, BF16>, la);
-    if (e != hipSuccess) return e;
-    k_decode_attend<D, BF16><<<routes, DA_THREADS, la, st>>>(s, pos, q, kc, vc, cos_t, sin_t, sel,
-                                                             out);
+    fn<<<routes, DS_THREADS, lds, st>>>(s, pos, q, kc, vc, cos_t, sin_t, cb, kbar, offsets,
+                                        entries, sel, out);
     return hipGetLastError();
 }
 
