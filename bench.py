@@ -209,10 +209,11 @@ def time_dense(cfg, reps=3, warmup=1):
 
 
 def run_decode(cfg, steps=20, warmup=3):
-    """Decode on a full cache of cfg.T tokens: mono_decode_step for the last
-    position (route + attend of B x Hq new-token queries) and mono_decode_index
-    re-indexing the last block (its summary and address, then the list
-    rebuild), each timed with HIP events on the launch stream; medians in us.
+    """Decode on a full cache of cfg.T tokens, the index holding its rotated-key
+    copy: mono_decode_step for the last position (route + attend of B x Hq
+    new-token queries) and mono_decode_index re-indexing the last block (its
+    summary, address and rotated keys, then the list rebuild), each timed with
+    HIP events on the launch stream; medians in us.
     Algorithmic bytes of a step: per (batch, kv-head) the key and value rows
     of the union of its heads' selected and local tokens, plus q, out and sel."""
     import torch
@@ -220,7 +221,7 @@ def run_decode(cfg, steps=20, warmup=3):
     d = synth.qkv_device(cfg)
     cos, sin = binding.device_rope(cfg)
     cb = torch.from_numpy(d["codebooks"]).cuda()
-    idx = binding.build_index(cfg, d["k"], cos, sin, cb)
+    idx = binding.build_index(cfg, d["k"], cos, sin, cb, rotated_keys=True)
     pos = cfg.T - 1
     q = d["q"][:, pos].contiguous()
     sel = torch.empty((cfg.B, cfg.Hq, cfg.R), dtype=torch.int32, device="cuda")

@@ -86,7 +86,13 @@ typedef struct {
  *   offsets  [B][Hkv][A+1]   int32  list a of (b, g) is entries[offsets[a] .. offsets[a+1])
  *   entries  [B][Hkv][NB]    int32  ascending source blocks per list; -1 past offsets[A]
  *   load     [B][Hkv][A]     int32  blocks assigned per address before the capacity clamp
- *   overflow [B][Hkv]        int32  blocks dropped by the clamp */
+ *   overflow [B][Hkv]        int32  blocks dropped by the clamp
+ *   k_rot    [B][T][Hkv][d]  dtype  optional (NULL: absent): the rotated keys of the
+ *            indexed blocks, rounded to the activation dtype.  mono_build_index and
+ *            mono_decode_index write the rows of the blocks they index when it is
+ *            present; mono_decode_step then reads the selected blocks' keys from it
+ *            instead of rotating the cache's, so it must have been present whenever
+ *            the covered blocks were indexed. */
 typedef struct {
     float *kbar;
     int32_t *addr;
@@ -94,6 +100,7 @@ typedef struct {
     int32_t *entries;
     int32_t *load;
     int32_t *overflow;
+    void *k_rot;
 } mono_index;
 
 /* Which call a workspace is for. */

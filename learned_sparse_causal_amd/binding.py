@@ -36,7 +36,7 @@ class MonoConfig(ctypes.Structure):
 
 class MonoIndex(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("kbar", "addr", "offsets", "entries", "load", "overflow")]
+                ("kbar", "addr", "offsets", "entries", "load", "overflow", "k_rot")]
 
 
 _lib = None
@@ -144,16 +144,22 @@ def device_rope(cfg, device="cuda", base=10000.0):
     return torch.from_numpy(c).to(device), torch.from_numpy(s).to(device)
 
 
-def empty_index(cfg, device="cuda"):
+def empty_index(cfg, device="cuda", rotated_keys=False):
+    """Index arrays for cfg; with rotated_keys the optional k_rot copy
+    [B, T, Hkv, d] (activation dtype) that the decode step reads."""
     torch = _torch()
     BG = (cfg.B, cfg.Hkv)
     i32 = torch.int32
-    return dict(kbar=torch.empty(BG + (cfg.NB, cfg.d), dtype=torch.float32, device=device),
-                addr=torch.empty(BG + (cfg.NB,), dtype=i32, device=device),
-                offsets=torch.empty(BG + (cfg.A + 1,), dtype=i32, device=device),
-                entries=torch.empty(BG + (cfg.NB,), dtype=i32, device=device),
-                load=torch.empty(BG + (cfg.A,), dtype=i32, device=device),
-                overflow=torch.empty(BG, dtype=i32, device=device))
+    idx = dict(kbar=torch.empty(BG + (cfg.NB, cfg.d), dtype=torch.float32, device=device),
+               addr=torch.empty(BG + (cfg.NB,), dtype=i32, device=device),
+               offsets=torch.empty(BG + (cfg.A + 1,), dtype=i32, device=device),
+               entries=torch.empty(BG + (cfg.NB,), dtype=i32, device=device),
+               load=torch.empty(BG + (cfg.A,), dtype=i32, device=device),
+               overflow=torch.empty(BG, dtype=i32, device=device))
+    if rotated_keys:
+        idx["k_rot"] = torch.empty((cfg.B, cfg.T, cfg.Hkv, cfg.d), dtype=_act_dtype(cfg),
+                                   device=device)
+    return idx
 
 
 def _index_struct(cfg, idx):
@@ -164,7 +170,9 @@ def _index_struct(cfg, idx):
                      _need(idx["offsets"], BG + (cfg.A + 1,), torch.int32, "offsets"),
                      _need(idx["entries"], BG + (cfg.NB,), torch.int32, "entries"),
                      _need(idx["load"], BG + (cfg.A,), torch.int32, "load"),
-                     _need(idx["overflow"], BG, torch.int32, "overflow"))
+                     _need(idx["overflow"], BG, torch.int32, "overflow"),
+                     _need(idx["k_rot"], (cfg.B, cfg.T, cfg.Hkv, cfg.d), _act_dtype(cfg), "k_rot")
+                     if idx.get("k_rot") is not None else None)
 
 
 def _workspace(cfg, which, ws):
@@ -179,11 +187,12 @@ def _workspace(cfg, which, ws):
     return ws, ws.numel()
 
 
-def build_index(cfg, k, rope_cos, rope_sin, codebooks, index=None):
-    """mono_build_index: returns the index dict (kbar, addr, offsets, entries, load, overflow)."""
+def build_index(cfg, k, rope_cos, rope_sin, codebooks, index=None, rotated_keys=False):
+    """mono_build_index: returns the index dict (kbar, addr, offsets, entries, load,
+    overflow, and k_rot when the index holds one or rotated_keys asks for it)."""
     torch = _torch()
     c = make_config(cfg)
-    idx = index if index is not None else empty_index(cfg)
+    idx = index if index is not None else empty_index(cfg, rotated_keys=rotated_keys)
     st = _index_struct(cfg, idx)
     args = (_need(k, (cfg.B, cfg.T, cfg.Hkv, cfg.d), _act_dtype(cfg), "k"),
             _need(rope_cos, (cfg.T, cfg.d // 2), torch.float32, "rope_cos"),

@@ -37,7 +37,7 @@ hipError_t launch_posting_lists_prefix(const Shape &s, int nbu, const int32_t *a
                                        int32_t *offsets, int32_t *entries, int32_t *load,
                                        int32_t *overflow, hipStream_t st);
 hipError_t launch_decode(const Shape &s, int pos, const void *q, const void *kc, const void *vc,
-                         const float *cos_t, const float *sin_t, const float *cb,
+                         const void *krot, const float *cos_t, const float *sin_t, const float *cb,
                          const float *kbar, const int32_t *offsets, const int32_t *entries,
                          int32_t *sel, void *out, hipStream_t st);
 size_t dense_ws_layout(const Shape &s, size_t *off);
@@ -251,7 +251,8 @@ mono_status mono_build_index(const mono_config *cfg, const void *k, const float 
     if (st != MONO_OK) return st;
     if (!k || !rope_cos || !rope_sin || !codebooks || !index_ok(out)) return MONO_ERR_NULL;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = launch_block_address(s, k, rope_cos, rope_sin, codebooks, out->kbar, out->addr, hs);
+    hipError_t e = launch_block_address(s, k, rope_cos, rope_sin, codebooks, out->kbar, out->addr, hs,
+                                        out->k_rot);
     if (e != hipSuccess) return MONO_ERR_HIP;
     e = launch_posting_lists(s, out->addr, out->offsets, out->entries, out->load, out->overflow, hs);
     return hip_status(e);
@@ -382,7 +383,7 @@ mono_status mono_decode_index(const mono_config *cfg, const void *k_cache, const
     if (n_indexed < 0 || n_indexed > nb) return MONO_ERR_SHAPE;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     if (launch_block_address_range(s, n_indexed, nb, k_cache, rope_cos, rope_sin, codebooks,
-                                   idx->kbar, idx->addr, hs) != hipSuccess)
+                                   idx->kbar, idx->addr, hs, idx->k_rot) != hipSuccess)
         return MONO_ERR_HIP;
     return hip_status(launch_posting_lists_prefix(s, nb, idx->addr, idx->offsets, idx->entries,
                                                   idx->load, idx->overflow, hs));
@@ -399,8 +400,8 @@ mono_status mono_decode_step(const mono_config *cfg, const void *q, const void *
         !sel || !out)
         return MONO_ERR_NULL;
     if (pos < 0 || pos >= s.T) return MONO_ERR_SHAPE;
-    return hip_status(launch_decode(s, pos, q, k_cache, v_cache, rope_cos, rope_sin, codebooks,
-                                    idx->kbar, idx->offsets, idx->entries, sel, out,
+    return hip_status(launch_decode(s, pos, q, k_cache, v_cache, idx->k_rot, rope_cos, rope_sin,
+                                    codebooks, idx->kbar, idx->offsets, idx->entries, sel, out,
                                     reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -433,6 +434,7 @@ mono_status mono_mixer_forward(const mono_config *cfg, const void *x, const void
     idx.entries = reinterpret_cast<int32_t *>(base + off[6]);
     idx.load = reinterpret_cast<int32_t *>(base + off[7]);
     idx.overflow = reinterpret_cast<int32_t *>(base + off[8]);
+    idx.k_rot = nullptr;
     int32_t *sel = reinterpret_cast<int32_t *>(base + off[9]);
     void *attn = base + off[10];
     void *inner = base + off[11];

@@ -22,6 +22,7 @@
 //   softmax, and the eight states are merged through LDS.
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -178,7 +179,8 @@ __device__ __forceinline__ void load_run(const void *base, size_t i, float (&x)[
 template <int D, int P, bool BF16>
 __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
     Shape s, int pos, const void *__restrict__ q, const void *__restrict__ kc,
-    const void *__restrict__ vc, const float *__restrict__ cos_t, const float *__restrict__ sin_t,
+    const void *__restrict__ vc, const void *__restrict__ krot, const float *__restrict__ cos_t,
+    const float *__restrict__ sin_t,
     const float *__restrict__ cb, const float *__restrict__ kbar,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ entries,
     int32_t *__restrict__ sel, void *__restrict__ out) {
@@ -292,15 +294,36 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
     const int jq = lane >> 4, pq = (lane & 15) * QPL;
     // bf16: every sub-pass's key words are loaded before the values
     constexpr int KJ = BF16 ? 4 : 1;
-    auto attend_item = [&](int it) {
+    // pre-rotated keys: lane part takes dims part D/4 .. part D/4 + D/4 - 1 of
+    // its key (bf16: NW 16-byte words)
+    constexpr int NW = D / 32;
+    auto attend_item = [&](int it, auto rotated) {
+        constexpr bool ROT = decltype(rotated)::value;
         const int bk = blk[it / per_blk];
         if (bk < 0) return;
         const int s0 = bk * s.beta + (it % per_blk) * WAVE;
         if (s0 > pos) return;
+        // key row of sub-pass j for this lane (keys past pos read row pos)
+        auto krow = [&](int j) { return base + (size_t)min(s0 + 16 * j + kq, pos) * rs + part * PPL; };
+        auto krow_r = [&](int j) { return base + (size_t)min(s0 + 16 * j + kq, pos) * rs + part * (D / 4); };
         // loads in the order they are waited for: the rotary rows (the
         // lane's keys' offsets kq, the query's s0 + 16 jq), the keys, then
         // the values
-        float rc[PPL], rsn[PPL];
+        float rc[ROT ? 1 : PPL], rsn[ROT ? 1 : PPL];
+        float cq[QPL], sq[QPL];
+        uint2 ku0[ROT ? 1 : KJ][NI], ku1[ROT ? 1 : KJ][NI];
+        u32x4 kw[ROT && BF16 ? 4 : 1][NW];
+        if constexpr (ROT) {
+            if constexpr (BF16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 *kr = reinterpret_cast<const u32x4 *>(
+                        reinterpret_cast<const u16 *>(krot) + krow_r(j));
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) kw[j][w] = kr[w];
+                }
+            }
+        } else {
 #pragma unroll
         for (int n = 0; n < NI; ++n) {
             const float4 c4 = *reinterpret_cast<const float4 *>(cos_t + (size_t)kq * H + part * PPL + 4 * n);
@@ -308,7 +331,6 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
             rc[4 * n] = c4.x; rc[4 * n + 1] = c4.y; rc[4 * n + 2] = c4.z; rc[4 * n + 3] = c4.w;
             rsn[4 * n] = s4.x; rsn[4 * n + 1] = s4.y; rsn[4 * n + 2] = s4.z; rsn[4 * n + 3] = s4.w;
         }
-        float cq[QPL], sq[QPL];
         {
             const size_t row = (size_t)min(s0 + 16 * jq, s.T - 1) * H + pq;   // unused past pos
 #pragma unroll
@@ -317,9 +339,6 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                 sq[e] = sin_t[row + e];
             }
         }
-        // key row of sub-pass j for this lane (keys past pos read row pos)
-        auto krow = [&](int j) { return base + (size_t)min(s0 + 16 * j + kq, pos) * rs + part * PPL; };
-        uint2 ku0[KJ][NI], ku1[KJ][NI];
         if constexpr (BF16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -330,6 +349,7 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                     ku1[j][n] = *reinterpret_cast<const uint2 *>(kr + 4 * n + H);
                 }
             }
+        }
         }
         // the item's value rows (this lane's dims); rows past pos read row
         // pos (p = 0 there)
@@ -349,21 +369,48 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                     vr[kk][j] = __float_as_uint(reinterpret_cast<const float *>(vc)[vo + j]);
             }
         }
-        // the query rotated back by s0 + 16 jq: (x c + y s, y c - x s)
+        if constexpr (!ROT) {
+            // the query rotated back by s0 + 16 jq: (x c + y s, y c - x s)
 #pragma unroll
-        for (int e = 0; e < QPL; ++e) {
-            const float x = qa[pq + e], y = qa[pq + e + H];
-            q_i[jq * D + pq + e] = x * cq[e] + y * sq[e];
-            q_i[jq * D + pq + e + H] = y * cq[e] - x * sq[e];
+            for (int e = 0; e < QPL; ++e) {
+                const float x = qa[pq + e], y = qa[pq + e + H];
+                q_i[jq * D + pq + e] = x * cq[e] + y * sq[e];
+                q_i[jq * D + pq + e + H] = y * cq[e] - x * sq[e];
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): q_i written
+            __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): q_i written
-        __builtin_amdgcn_wave_barrier();
         float lg[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int key = s0 + 16 * j + kq;
             const float *qj = q_i + j * D + part * PPL;
             float acc = 0.0f;
+            if constexpr (ROT && BF16) {
+                // pre-rotated bf16 keys, unpacked; fp32 fused multiply-adds
+                const float *qd = qa + part * (D / 4);
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t kp = kw[j][w][e];
+                        acc = fmaf(qd[8 * w + 2 * e], __uint_as_float(kp << 16), acc);
+                        acc = fmaf(qd[8 * w + 2 * e + 1], __uint_as_float(kp & 0xFFFF0000u), acc);
+                    }
+                }
+            } else if constexpr (ROT) {
+                const float4 *kr = reinterpret_cast<const float4 *>(
+                    reinterpret_cast<const float *>(krot) + krow_r(j));
+                const float *qd = qa + part * (D / 4);
+#pragma unroll
+                for (int w = 0; w < D / 16; ++w) {
+                    const float4 k4 = kr[w];
+                    acc = fmaf(qd[4 * w], k4.x, acc);
+                    acc = fmaf(qd[4 * w + 1], k4.y, acc);
+                    acc = fmaf(qd[4 * w + 2], k4.z, acc);
+                    acc = fmaf(qd[4 * w + 3], k4.w, acc);
+                }
+            } else {
 #pragma unroll
             for (int n = 0; n < NI; ++n) {
                 float x0[4], x1[4];
@@ -388,6 +435,7 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                     acc = fmaf(qj[4 * n + e], k0, acc);
                     acc = fmaf(qj[4 * n + e + H], k1, acc);
                 }
+            }
             }
             // sum over the lane quad
             acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, false));
@@ -638,11 +686,16 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
         }
     } else {
         // the local blocks, while wave 0 routes
-        for (int it = wave - 1; it < nloc_items; it += DS_WAVES - 1) attend_item(it);
+        for (int it = wave - 1; it < nloc_items; it += DS_WAVES - 1)
+            attend_item(it, std::false_type{});
     }
     __syncthreads();
     // the selected blocks, on every wave
-    for (int it = nloc_items + wave; it < nitems; it += DS_WAVES) attend_item(it);
+    // (covered by the index, so pre-rotated when it holds rotated keys)
+    for (int it = nloc_items + wave; it < nitems; it += DS_WAVES) {
+        if (krot) attend_item(it, std::true_type{});
+        else attend_item(it, std::false_type{});
+    }
 
     // merge the waves' states
     if (lane == 0) {
@@ -679,7 +732,8 @@ hipError_t lds_at_least(F *fn, size_t bytes) {
 
 template <int D, bool BF16>
 hipError_t run_decode(const Shape &s, int pos, const void *q, const void *kc, const void *vc,
-                      const float *cos_t, const float *sin_t, const float *cb, const float *kbar,
+                      const void *krot, const float *cos_t, const float *sin_t, const float *cb,
+                      const float *kbar,
                       const int32_t *offsets, const int32_t *entries, int32_t *sel, void *out,
                       hipStream_t st) {
     const unsigned routes = (unsigned)(s.B * s.Hq);
@@ -687,7 +741,7 @@ hipError_t run_decode(const Shape &s, int pos, const void *q, const void *kc, co
     auto *fn = s.P == 1 ? k_decode_step<D, 1, BF16> : k_decode_step<D, 2, BF16>;
     const hipError_t e = lds_at_least(fn, lds);
     if (e != hipSuccess) return e;
-    fn<<<routes, DS_THREADS, lds, st>>>(s, pos, q, kc, vc, cos_t, sin_t, cb, kbar, offsets,
+    fn<<<routes, DS_THREADS, lds, st>>>(s, pos, q, kc, vc, krot, cos_t, sin_t, cb, kbar, offsets,
                                         entries, sel, out);
     return hipGetLastError();
 }
@@ -695,17 +749,17 @@ hipError_t run_decode(const Shape &s, int pos, const void *q, const void *kc, co
 }  // namespace
 
 hipError_t launch_decode(const Shape &s, int pos, const void *q, const void *kc, const void *vc,
-                         const float *cos_t, const float *sin_t, const float *cb,
+                         const void *krot, const float *cos_t, const float *sin_t, const float *cb,
                          const float *kbar, const int32_t *offsets, const int32_t *entries,
                          int32_t *sel, void *out, hipStream_t st) {
     const bool bf = s.dtype == 1;
     if (s.d == 64)
-        return bf ? run_decode<64, true>(s, pos, q, kc, vc, cos_t, sin_t, cb, kbar, offsets,
+        return bf ? run_decode<64, true>(s, pos, q, kc, vc, krot, cos_t, sin_t, cb, kbar, offsets,
                                          entries, sel, out, st)
-                  : run_decode<64, false>(s, pos, q, kc, vc, cos_t, sin_t, cb, kbar, offsets,
+                  : run_decode<64, false>(s, pos, q, kc, vc, krot, cos_t, sin_t, cb, kbar, offsets,
                                           entries, sel, out, st);
-    return bf ? run_decode<128, true>(s, pos, q, kc, vc, cos_t, sin_t, cb, kbar, offsets, entries,
-                                      sel, out, st)
-              : run_decode<128, false>(s, pos, q, kc, vc, cos_t, sin_t, cb, kbar, offsets,
+    return bf ? run_decode<128, true>(s, pos, q, kc, vc, krot, cos_t, sin_t, cb, kbar, offsets,
+                                      entries, sel, out, st)
+              : run_decode<128, false>(s, pos, q, kc, vc, krot, cos_t, sin_t, cb, kbar, offsets,
                                        entries, sel, out, st);
 }

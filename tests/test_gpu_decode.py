@@ -9,7 +9,10 @@ oracle.
   route (selected ids bit for bit, near-ties excused as for mono_route) and
   attention (fp32 within 1e-4 max abs, bf16 within 2e-2 max relative per
   (batch, head)), with the index grown by mono_decode_index or built by
-  mono_build_index over the same layout.
+  mono_build_index over the same layout, with and without the index's
+  rotated-key copy (which the step then reads for the selected blocks).
+- That copy holds, for every indexed block and no other, the keys rotated in
+  fp32 (products rounded before the add) and rounded to the activation dtype.
 """
 import numpy as np
 import pytest
@@ -76,6 +79,46 @@ def test_decode_index_grows_like_prefix_builds(orc, cfg):
         assert g["overflow"].sum() > 0
 
 
+def expected_rotated_keys(cfg, k, cos, sin):
+    """Keys [B, T, Hkv, d] rotated in fp32 (each product rounded before the
+    add), rounded to the activation dtype (round to nearest even)."""
+    t = torch()
+    x = t.from_numpy(np.ascontiguousarray(k, dtype=np.float32))
+    c = t.from_numpy(cos)[None, :, None, :]
+    s = t.from_numpy(sin)[None, :, None, :]
+    h = cfg.d // 2
+    x0, x1 = x[..., :h], x[..., h:]
+    r = t.cat([x0 * c - x1 * s, x1 * c + x0 * s], dim=-1)
+    return r.to(t.bfloat16).float().numpy() if cfg.dtype == "bf16" else r.numpy()
+
+
+ROT_CFGS = [configs.SMALL.with_(name="gqa_T2048", T=2048, Hq=6, Hkv=2),
+            configs.SMALL.with_(name="d128_beta128_f32", d=128, beta=128, T=4096, Hq=4, Hkv=1,
+                                R=8, dtype="f32")]
+
+
+@pytest.mark.parametrize("cfg", ROT_CFGS, ids=lambda c: c.name)
+def test_decode_index_writes_rotated_keys(cfg):
+    say("[decode index, rotated keys] %s" % cfg.name)
+    t = torch()
+    inp, d = small_inputs(cfg)
+    cos, sin = binding.device_rope(cfg)
+    cb = t.from_numpy(inp["codebooks"]).cuda()
+    idx = binding.empty_index(cfg, rotated_keys=True)
+    idx["k_rot"].fill_(7.0)                          # sentinel for rows not indexed
+    want = expected_rotated_keys(cfg, inp["k"], host(cos), host(sin))
+    done = 0
+    for n_tok in (3 * cfg.beta + 5, 8 * cfg.beta, cfg.T):
+        binding.decode_index(cfg, d["k"], cos, sin, cb, idx, done, n_tok)
+        done = n_tok // cfg.beta
+        got = host(idx["k_rot"])
+        T_ix = done * cfg.beta
+        assert np.array_equal(got[:, :T_ix], want[:, :T_ix])
+        assert (got[:, T_ix:] == 7.0).all()
+    full = binding.build_index(cfg, d["k"], cos, sin, cb, rotated_keys=True)
+    assert np.array_equal(host(full["k_rot"]), want)
+
+
 def decode_positions(cfg, rng, n_random):
     beta, L, R = cfg.beta, cfg.L, cfg.R
     first_search = (R + L) * beta                     # first position with E > R
@@ -135,16 +178,17 @@ STEP_CFGS = [configs.TINY,
              configs.SMALL.with_(name="P1_K64", T=2048, P=1, K=64, Hq=4, Hkv=2)]
 
 
+@pytest.mark.parametrize("rotated", [False, True], ids=["raw_keys", "rotated_keys"])
 @pytest.mark.parametrize("cfg", STEP_CFGS, ids=lambda c: c.name)
-def test_decode_steps_match_whole_sequence_rows(orc, cfg):
-    say("[decode step] %s" % cfg.name)
+def test_decode_steps_match_whole_sequence_rows(orc, cfg, rotated):
+    say("[decode step] %s %s" % (cfg.name, "rotated keys" if rotated else "raw keys"))
     t = torch()
     inp, d = small_inputs(cfg)
     positions = decode_positions(cfg, np.random.default_rng(21), 12)
     o_idx, ids, o_sel, gaps, o_out = oracle_rows(orc, cfg, inp, positions)
     cos, sin = binding.device_rope(cfg)
     cb = t.from_numpy(inp["codebooks"]).cuda()
-    idx = binding.empty_index(cfg)
+    idx = binding.empty_index(cfg, rotated_keys=rotated)
     g_sel = np.empty((cfg.B, cfg.Hq, len(positions), cfg.R), np.int32)
     g_out = np.empty((cfg.B, cfg.Hq, len(positions), cfg.d), np.float32)
     done = 0
@@ -191,29 +235,36 @@ def test_decode_step_all_eligible(orc):
 
 def test_decode_step_large_with_prefill_index(orc):
     """Largest workload (batch 8, 64K-token cache, d 128): the index built by
-    mono_build_index over the whole cache, decode steps at the last position
-    and two others, every (batch, head), against the oracle's rows."""
+    mono_build_index over the whole cache (with and without its rotated-key
+    copy), decode steps at the last position and two others, every
+    (batch, head), against the oracle's rows."""
     cfg = configs.LARGE
     say("[decode step] %s" % cfg.name)
     t = torch()
     d = synth.qkv_device(cfg)
     cos, sin = binding.device_rope(cfg)
     cb = t.from_numpy(d["codebooks"]).cuda()
-    idx = binding.build_index(cfg, d["k"], cos, sin, cb)
     positions = np.array([cfg.T // 2 + 77, cfg.T - cfg.beta, cfg.T - 1])
-    g_sel = np.empty((cfg.B, cfg.Hq, len(positions), cfg.R), np.int32)
-    g_out = np.empty((cfg.B, cfg.Hq, len(positions), cfg.d), np.float32)
-    for i, pos in enumerate(positions):
-        sel, out = binding.decode_step(cfg, d["q"][:, pos].contiguous(), d["k"], d["v"], cos, sin,
-                                       cb, idx, int(pos))
-        g_sel[:, :, i] = host(sel)
-        g_out[:, :, i] = host(out)
+    results = {}
+    for rotated in (False, True):
+        idx = binding.build_index(cfg, d["k"], cos, sin, cb, rotated_keys=rotated)
+        g_sel = np.empty((cfg.B, cfg.Hq, len(positions), cfg.R), np.int32)
+        g_out = np.empty((cfg.B, cfg.Hq, len(positions), cfg.d), np.float32)
+        for i, pos in enumerate(positions):
+            sel, out = binding.decode_step(cfg, d["q"][:, pos].contiguous(), d["k"], d["v"], cos,
+                                           sin, cb, idx, int(pos))
+            g_sel[:, :, i] = host(sel)
+            g_out[:, :, i] = host(out)
+        results[rotated] = (g_sel, g_out)
+        del idx
     inp = {k: host(d[k]) for k in ("q", "k", "v")}
     inp["codebooks"] = d["codebooks"]
     o_idx, ids, o_sel, gaps, o_out = oracle_rows(orc, cfg, inp, positions)
-    n, worst = compare_decode(cfg, o_idx, ids, o_sel, gaps, o_out, g_sel.reshape(-1, cfg.R),
-                              g_out.reshape(-1, cfg.d))
-    say("  %d routes: %d excused, attention error %.3g" % (len(ids), n, worst))
+    for rotated, (g_sel, g_out) in results.items():
+        n, worst = compare_decode(cfg, o_idx, ids, o_sel, gaps, o_out, g_sel.reshape(-1, cfg.R),
+                                  g_out.reshape(-1, cfg.d))
+        say("  %s: %d routes, %d excused, attention error %.3g"
+            % ("rotated keys" if rotated else "raw keys", len(ids), n, worst))
 
 
 def test_decode_overflowed_lists():
