@@ -78,27 +78,55 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t k, int src) {
     return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t k, int m) {
-    const int lo = __shfl_xor((int)(uint32_t)k, m), hi = __shfl_xor((int)(uint32_t)(k >> 32), m);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+// The value lane ^ J holds (J a power of two below 64), without the LDS
+// crossbar: DPP quad permutes for 1 and 2, a row shift each way for 4 and 8
+// (row_shl: lane + J, row_shr: lane - J), the gfx950 swaps for 16 and 32
+// (of the returned pair, the even half-row / half-wave gets the partner in
+// the second element, the odd one in the first).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
+    if constexpr (J == 1) {
+        return __builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    } else if constexpr (J == 2) {
+        return __builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    } else if constexpr (J == 4 || J == 8) {
+        const uint32_t up = __builtin_amdgcn_mov_dpp((int)x, 0x100 + J, 0xF, 0xF, false);
+        const uint32_t dn = __builtin_amdgcn_mov_dpp((int)x, 0x110 + J, 0xF, 0xF, false);
+        return (lane & J) ? dn : up;
+    } else if constexpr (J == 16) {
+        const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? a[0] : a[1];
+    } else {
+        static_assert(J == 32, "lane distance");
+        const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? a[0] : a[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t k, int lane) {
+    const uint32_t lo = xor_lane<J>((uint32_t)k, lane), hi = xor_lane<J>((uint32_t)(k >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One bitonic compare-exchange (runs of SIZE, partner distance J), then the
+// rest of the network.
+template <int SEG, int SIZE, int J>
+__device__ __forceinline__ uint64_t bitonic_from(uint64_t k, int i, int lane) {
+    const uint64_t o = xor_lane_u64<J>(k, lane);
+    // in a descending run the lower lane of a pair keeps the larger key
+    const bool keep_max = ((i & J) == 0) == ((i & SIZE) == 0);
+    k = keep_max ? key_max(k, o) : (k < o ? k : o);
+    if constexpr (J > 1) return bitonic_from<SEG, SIZE, J / 2>(k, i, lane);
+    else if constexpr (SIZE < SEG) return bitonic_from<SEG, 2 * SIZE, SIZE>(k, i, lane);
+    else return k;
 }
 
 // Bitonic sort of one key per lane, largest first, within aligned groups of
 // SEG lanes (a power of two <= 64).
 template <int SEG>
 __device__ __forceinline__ uint64_t sort_desc(uint64_t k, int lane) {
-    const int i = lane & (SEG - 1);
-#pragma unroll
-    for (int size = 2; size <= SEG; size <<= 1) {
-#pragma unroll
-        for (int j = size >> 1; j > 0; j >>= 1) {
-            const uint64_t o = shfl_xor_u64(k, j);
-            // in a descending run the lower lane of a pair keeps the larger key
-            const bool keep_max = ((i & j) == 0) == ((i & size) == 0);
-            k = keep_max ? key_max(k, o) : (k < o ? k : o);
-        }
-    }
-    return k;
+    return bitonic_from<SEG, 2, 1>(k, lane & (SEG - 1), lane);
 }
 
 // fp32 fused multiply-add chain over n = N elements in index order, with the
@@ -524,6 +552,49 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                     if (msk != ~0ull) break;   // a later block ends the prefix
                 }
             };
+            // Lists a_0, a_1, ... (lane r holds a_r, or a < 0 for none) taken
+            // in that order at once: each lane finds its list's eligible
+            // prefix by binary search (entries ascend), a wave scan places
+            // the prefixes, and with stop_at > 0 only the lists up to the
+            // first at which stop_at blocks were collected are taken (the
+            // walk's stopping rule); then the wave copies them.
+            auto take_lists = [&](int a, int stop_at) {
+                // lists are in lanes 0..15 (n_probes <= 16, and R <= 16 when
+                // the search runs): a DPP scan within that row
+                int e0 = 0, cnt = 0;
+                if (a >= 0) {
+                    e0 = off[a];
+                    int lo2 = e0, hi2 = off[a + 1];
+                    while (lo2 < hi2) {
+                        const int mid = (lo2 + hi2) >> 1;
+                        if (ent[mid] <= last) lo2 = mid + 1;
+                        else hi2 = mid;
+                    }
+                    cnt = lo2 - e0;
+                }
+                int incl = cnt;   // row_shr:1, 2, 4, 8 with zeros from outside the row
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);
+                incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);
+                int nl = 16;                         // lists taken
+                if (stop_at > 0) {
+                    const uint64_t reach = __ballot(lane < 16 && incl >= stop_at);
+                    if (reach) nl = __ffsll((long long)reach);   // through the first that reaches it
+                }
+                const int excl = incl - cnt;
+                uint64_t todo = __ballot(lane < nl && cnt > 0);
+                while (todo) {
+                    const int r = __ffsll((long long)todo) - 1;
+                    todo &= todo - 1;
+                    const int cr = __builtin_amdgcn_readlane(cnt, r);
+                    const int er = __builtin_amdgcn_readlane(e0, r);
+                    const int pr = npool + __builtin_amdgcn_readlane(excl, r);
+                    for (int x = lane; x < cr; x += WAVE)
+                        if (pr + x < NB) pool_n[pr + x] = ent[er + x];   // a valid index holds <= NB blocks
+                }
+                npool = min(NB, npool + __builtin_amdgcn_readlane(incl, nl - 1));
+            };
             // address sum, component 0 first (mixed radix, component 0 most significant)
             auto sigma = [&](int c0, int c1) { return P == 1 ? sc[c0] : sc[c0] + sc[K + c1]; };
             // The walk over addresses in (sum desc, address asc) order stops at
@@ -545,7 +616,7 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                     const int c = lane & 31, p = lane >> 5;
                     const uint64_t ks = sort_desc<32>(c < K ? order_key(sc[p * K + c], c) : 0ull, lane);
                     k0 = ks;                         // lanes 0..31: component 0
-                    k1 = shfl_xor_u64(ks, 32);       // lanes 0..31: component 1
+                    k1 = xor_lane_u64<32>(ks, lane);  // lanes 0..31: component 1
                 } else {
                     k0 = sort_desc<64>(lane < K ? order_key(sc[lane], lane) : 0ull, lane);
                     k1 = sort_desc<64>(lane < K ? order_key(sc[K + lane], lane) : 0ull, lane);
@@ -564,14 +635,15 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                 const bool ok = px >= 0 && kx != 0ull && ky != 0ull;
                 wk = sort_desc<64>(ok ? order_key(sigma(c0, c1), c0 * K + c1) : 0ull, lane);
             }
-            for (int r = 0; r < np1; ++r) take(key_id(shfl_u64(wk, r)));
+            take_lists(lane < np1 ? key_id(wk) : -1, 0);
             const uint64_t prev = shfl_u64(wk, np1 - 1);   // key of the last visited address
             const int npool1 = npool;
             const float *kb = kbar + u * (size_t)NB * D;
-            // the summary rows of the first 64 pooled blocks, in flight during
-            // the extension (lanes without a block read row 0)
+            // the summary rows of the first 64 pooled blocks (their first 64
+            // dimensions at d = 128), in flight during the extension (lanes
+            // without a block read row 0)
             constexpr bool PREFETCH = BF16 || D == 64;
-            constexpr int KPW = PREFETCH ? D / 4 : 1;
+            constexpr int KPW = PREFETCH ? 16 : 1;
             float4 kpre[KPW];
             if constexpr (PREFETCH) {
                 const float4 *kr = reinterpret_cast<const float4 *>(
@@ -589,41 +661,79 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                 // lane's address a0 + lane as codes (c0, c1), advanced by 64 per step
                 int c0 = P == 1 ? lane : lane / K, c1 = P == 1 ? 0 : lane % K;
                 const int s0 = P == 1 ? WAVE : WAVE / K, s1 = P == 1 ? 0 : WAVE % K;
-                for (int a0 = 0; a0 < A; a0 += WAVE) {
-                    const int a = a0 + lane;
-                    bool ok = false;
-                    float sg = 0.0f;
-                    if (a < A) {
-                        const int e0 = off[a];
-                        if (e0 < off[a + 1] && ent[e0] <= last) {
-                            sg = sigma(c0, c1);
-                            ok = order_key(sg, a) < prev;
+                // SB steps at a time: their list offsets and sums are read
+                // together, then their lists' first entries
+                constexpr int SB = 8;
+                for (int a0 = 0; a0 < A; a0 += SB * WAVE) {
+                    int e0[SB], e1[SB], f[SB];
+                    float sa[SB];
+#pragma unroll
+                    for (int u = 0; u < SB; ++u) {
+                        const int a = a0 + u * WAVE + lane;
+                        const int ac = min(a, A - 1);
+                        e0[u] = off[ac];
+                        e1[u] = off[ac + 1];
+                        sa[u] = a < A ? sigma(c0, c1) : 0.0f;
+                        c0 += s0;
+                        c1 += s1;
+                        if (P == 2 && c1 >= K) { c1 -= K; ++c0; }
+                    }
+#pragma unroll
+                    for (int u = 0; u < SB; ++u) f[u] = e0[u] < e1[u] ? ent[e0[u]] : INT_MAX;
+#pragma unroll
+                    for (int u = 0; u < SB; ++u) {
+                        const int a = a0 + u * WAVE + lane;
+                        const bool ok = a < A && f[u] <= last && order_key(sa[u], a) < prev;
+                        const uint64_t msk = __ballot(ok);
+                        if (ok) {
+                            const int x = ncand + __popcll(msk & lanemask);
+                            cand[x] = a;
+                            sig[x] = sa[u];
                         }
+                        ncand += __popcll(msk);
                     }
-                    const uint64_t msk = __ballot(ok);
-                    if (ok) {
-                        const int x = ncand + __popcll(msk & lanemask);
-                        cand[x] = a;
-                        sig[x] = sg;
-                    }
-                    ncand += __popcll(msk);
-                    c0 += s0;
-                    c1 += s1;
-                    if (P == 2 && c1 >= K) { c1 -= K; ++c0; }
                 }
                 __builtin_amdgcn_s_waitcnt(0xc07f);
                 __builtin_amdgcn_wave_barrier();
-                uint64_t pv = prev;
-                while (npool < R) {
-                    uint64_t best = 0;
-                    for (int x = lane; x < ncand; x += WAVE) {
-                        const uint64_t k = order_key(sig[x], cand[x]);
-                        if (k < pv) best = key_max(best, k);
+                // rounds: with at most NKR candidates per lane their keys stay
+                // in registers (a taken key is cleared; keys are distinct)
+                constexpr int NKR = 8;
+                if (ncand <= NKR * WAVE) {
+                    uint64_t ck[NKR];
+#pragma unroll
+                    for (int t = 0; t < NKR; ++t) {
+                        const int x = lane + t * WAVE;
+                        ck[t] = x < ncand ? order_key(sig[x], cand[x]) : 0ull;
                     }
-                    best = wave_max_key(best);
-                    if (best == 0) break;                    // every list taken
-                    pv = best;
-                    take(key_id(best));
+                    // every candidate list holds an eligible block, so the
+                    // walk ends within the R - npool best: pick them in
+                    // order (lane r keeps the r-th), then take them at once
+                    const int need = R - npool;
+                    uint64_t mine = 0;
+                    for (int r = 0; r < need; ++r) {
+                        uint64_t best = 0;
+#pragma unroll
+                        for (int t = 0; t < NKR; ++t) best = key_max(best, ck[t]);
+                        best = wave_max_key(best);
+                        if (best == 0) break;                // every list picked
+#pragma unroll
+                        for (int t = 0; t < NKR; ++t) ck[t] = ck[t] == best ? 0ull : ck[t];
+                        if (lane == r) mine = best;
+                    }
+                    take_lists(mine ? key_id(mine) : -1, need);
+                } else {
+                    uint64_t pv = prev;
+                    while (npool < R) {
+                        uint64_t best = 0;
+                        for (int x = lane; x < ncand; x += WAVE) {
+                            const uint64_t k = order_key(sig[x], cand[x]);
+                            if (k < pv) best = key_max(best, k);
+                        }
+                        best = wave_max_key(best);
+                        if (best == 0) break;                // every list taken
+                        pv = best;
+                        take(key_id(best));
+                    }
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -632,13 +742,19 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
             for (int x = lane; x < npool; x += WAVE) {
                 float acc;
                 if (PREFETCH && x == lane && lane < npool1) {
+                    const float4 *kr = reinterpret_cast<const float4 *>(kb + (size_t)pool_n[x] * D);
+                    constexpr int NR = D / 4 - KPW > 0 ? D / 4 - KPW : 1;
+                    float4 rest[NR];
+#pragma unroll
+                    for (int j = KPW; j < D / 4; ++j) rest[j - KPW] = kr[j];
                     acc = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < KPW; ++j) {
-                        acc = fmaf(qr[4 * j], kpre[j].x, acc);
-                        acc = fmaf(qr[4 * j + 1], kpre[j].y, acc);
-                        acc = fmaf(qr[4 * j + 2], kpre[j].z, acc);
-                        acc = fmaf(qr[4 * j + 3], kpre[j].w, acc);
+                    for (int j = 0; j < D / 4; ++j) {
+                        const float4 kv = j < KPW ? kpre[j] : rest[j - KPW];
+                        acc = fmaf(qr[4 * j], kv.x, acc);
+                        acc = fmaf(qr[4 * j + 1], kv.y, acc);
+                        acc = fmaf(qr[4 * j + 2], kv.z, acc);
+                        acc = fmaf(qr[4 * j + 3], kv.w, acc);
                     }
                 } else {
                     acc = chain_lds_global<D>(qr, kb + (size_t)pool_n[x] * D);
