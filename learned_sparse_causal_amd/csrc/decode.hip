@@ -633,7 +633,10 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                 const uint64_t kx = shfl_u64(k0, max(px, 0)), ky = shfl_u64(k1, py);
                 const int c0 = key_id(kx), c1 = key_id(ky);
                 const bool ok = px >= 0 && kx != 0ull && ky != 0ull;
-                wk = sort_desc<64>(ok ? order_key(sigma(c0, c1), c0 * K + c1) : 0ull, lane);
+                const uint64_t pk = ok ? order_key(sigma(c0, c1), c0 * K + c1) : 0ull;
+                // the pairs fill lanes 0 .. npairs-1: sort only those
+                const int npairs = WAVE - __popcll(__ballot(px < 0));
+                wk = npairs <= 32 ? sort_desc<32>(pk, lane) : sort_desc<64>(pk, lane);
             }
             take_lists(lane < np1 ? key_id(wk) : -1, 0);
             const uint64_t prev = shfl_u64(wk, np1 - 1);   // key of the last visited address
@@ -769,8 +772,9 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
             const int nsel = min(R, npool);
             int mine = -1;
             if (npool <= WAVE) {
-                const uint64_t k = sort_desc<64>(
-                    lane < npool ? order_key(pool_r[lane], pool_n[lane]) : 0ull, lane);
+                const uint64_t k0 = lane < npool ? order_key(pool_r[lane], pool_n[lane]) : 0ull;
+                const uint64_t k = npool <= 16 ? sort_desc<16>(k0, lane)
+                                   : npool <= 32 ? sort_desc<32>(k0, lane) : sort_desc<64>(k0, lane);
                 if (lane < nsel) mine = key_id(k);
             } else {
                 uint64_t pprev = ~0ull;
