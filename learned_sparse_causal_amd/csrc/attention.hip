@@ -610,20 +610,72 @@ __device__ __forceinline__ int bin_start_of(const int32_t *bin_local, const int3
     return wg_base[2 * (bin / BIN_WG)] + bin_local[bin];
 }
 
+// Workgroup totals the scatter scans itself (into LDS) instead of reading
+// the separate scan's result: at most this many (16 KB of LDS).
+constexpr int SCATTER_SCAN_MAX = 2048;
+
 // Scatter (query, slot) ids into bin order and replace each entry's rank by
 // its list position (where its partial state will be written); threads
-// below nbins also write their bin's entries of the chunk table.
+// below nbins also write their bin's entries of the chunk table.  With
+// SCAN, every workgroup first forms the exclusive scan of the binsum
+// workgroup totals (wg_sum, nwg pairs) in LDS; else wg_sum already holds it.
+template <bool SCAN>
 __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbins,
                                                       const int32_t *__restrict__ sel,
                                                       int32_t *__restrict__ entry_pos,
                                                       const int32_t *__restrict__ bin_local,
                                                       const int32_t *__restrict__ chunk_local,
-                                                      const int32_t *__restrict__ wg_base,
+                                                      const int32_t *__restrict__ wg_sum,
                                                       const int32_t *__restrict__ seg_rel,
                                                       int32_t *__restrict__ list_q,
                                                       int4 *__restrict__ chunk_desc,
                                                       int grid_r, int32_t *__restrict__ wg_first) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    __shared__ int32_t base_s[SCAN ? 2 * SCATTER_SCAN_MAX + 2 : 1];
+    const int32_t *wg_base = wg_sum;
+    if constexpr (SCAN) {
+        // thread t owns totals [t * per, t * per + per); a workgroup scan of
+        // its sums places them (same arithmetic as k_attn_scan)
+        __shared__ int32_t ws[4], wc[4];
+        const int nwg = (nbins + BIN_WG - 1) / BIN_WG;
+        const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+        const int per = (nwg + 255) / 256;
+        const int lo = min(nwg, tid * per), hi = min(nwg, lo + per);
+        int s0 = 0, c0 = 0;
+        for (int k = lo; k < hi; ++k) {
+            s0 += wg_sum[2 * k];
+            c0 += wg_sum[2 * k + 1];
+        }
+        int ps = s0, pc = c0;
+#pragma unroll
+        for (int dlt = 1; dlt < WAVE; dlt <<= 1) {
+            const int a = __shfl_up(ps, dlt), c = __shfl_up(pc, dlt);
+            if (lane >= dlt) { ps += a; pc += c; }
+        }
+        if (lane == WAVE - 1) { ws[wv] = ps; wc[wv] = pc; }
+        __syncthreads();
+        int bs = 0, bc = 0, ts = 0, tc = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            bs += w < wv ? ws[w] : 0;
+            bc += w < wv ? wc[w] : 0;
+            ts += ws[w];
+            tc += wc[w];
+        }
+        int rs = bs + ps - s0, rc = bc + pc - c0;
+        for (int k = lo; k < hi; ++k) {
+            base_s[2 * k] = rs;
+            base_s[2 * k + 1] = rc;
+            rs += wg_sum[2 * k];
+            rc += wg_sum[2 * k + 1];
+        }
+        if (tid == 0) {
+            base_s[2 * nwg] = ts;
+            base_s[2 * nwg + 1] = tc;
+        }
+        __syncthreads();
+        wg_base = base_s;
+    }
     if (i < nbins) {
         // descriptors {bin, first row, end row} of the bin's chunks
         const long nb = (long)nbins;
@@ -1418,14 +1470,16 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
            (size_t)s.NB * sizeof(int), st>>>(s, sel, w.cnt, w.entry_pos, w.tile_flag, nseg);
     k_attn_binsum<<<dim3((unsigned)nwg), BIN_WG, 0, st>>>(nbins, nseg, s.NB, w.cnt, w.seg_rel,
                                                           w.bin_local, w.chunk_local, w.wg_sum);
-    k_attn_scan<<<1, 1024, 0, st>>>(nwg, w.wg_sum);
+    const bool scan_in_scatter = nwg <= SCATTER_SCAN_MAX;
+    if (!scan_in_scatter) k_attn_scan<<<1, 1024, 0, st>>>(nwg, w.wg_sum);
     const size_t lds_r = (size_t)((BETA / 64) * (T::K_ELEMS + T::V_ELEMS)) * sizeof(E);
     err = ensure_lds(k_attn_remote<D, BETA, BF16>, lds_r);
     if (err != hipSuccess) return err;
     const unsigned grid_r = std::min<unsigned>(
         persistent_grid(k_attn_remote<D, BETA, BF16>, lds_r, max_chunks(s)), MAX_REMOTE_GRID);
     const long nscat = std::max<long>(nent, nbins);
-    k_attn_scatter<<<dim3((unsigned)((nscat + 255) / 256)), 256, 0, st>>>(
+    auto *scatter = scan_in_scatter ? k_attn_scatter<true> : k_attn_scatter<false>;
+    scatter<<<dim3((unsigned)((nscat + 255) / 256)), 256, 0, st>>>(
         s, nseg, nbins, sel, w.entry_pos, w.bin_local, w.chunk_local, w.wg_sum, w.seg_rel,
         w.list_q, w.chunk_desc, (int)grid_r, w.wg_first);
     err = hipGetLastError();
