@@ -145,6 +145,36 @@ __device__ __forceinline__ float chain_lds_global(const float *a, const float *_
     return acc;
 }
 
+// The router's walk window: M, and per lane the pair (x, y) of code ranks
+// it scores (x | y << 8; 0xFFFF for none), the pairs with (x+1)(y+1) <= M,
+// x-major.  A per-configuration constant, made on the host.
+struct WalkPairs {
+    int M;
+    unsigned short xy[64];
+};
+
+WalkPairs walk_pairs(const Shape &s) {
+    WalkPairs w;
+    const int A = s.A, K = s.K, np1 = std::min(A, s.npr);
+    auto count = [&](int m) {
+        int c = 0;
+        for (int x = 0; x < std::min(m, K); ++x) c += std::min(m / (x + 1), K);
+        return c;
+    };
+    int M = np1;
+    if (s.P == 1) {
+        M = std::min(A, np1 + 16);
+    } else {
+        while (M < std::min(A, np1 + 16) && count(M + 1) <= 64) ++M;
+    }
+    w.M = M;
+    int l = 0;
+    for (int x = 0; x < std::min(M, K) && s.P == 2; ++x)
+        for (int y = 0; y < std::min(M / (x + 1), K) && l < 64; ++y) w.xy[l++] = (unsigned short)(x | y << 8);
+    for (; l < 64; ++l) w.xy[l] = 0xFFFF;
+    return w;
+}
+
 constexpr int DS_THREADS = 512;   // one workgroup per route
 constexpr int DS_WAVES = DS_THREADS / WAVE;
 
@@ -152,15 +182,15 @@ constexpr int DS_WAVES = DS_THREADS / WAVE;
 // query [d], per-wave probabilities [W][64], (m, l) [W][2], outputs [W][d],
 // back-rotated queries [W][4][d], blocks [L + R].  Route part: the rotated
 // query [d], code scores [P K], list offsets [A + 1], entries [NB], pool ids
-// [NB], then one area that holds the extension's addresses and their sums
-// ([min(A, NB)] each) and, once the extension is done, the pool's rerank
-// scores [NB].
+// [NB], the pool's rerank scores [NB], the addresses whose list holds an
+// eligible block [min(A, NB)] (as packed codes), and two counters (those
+// addresses, the waves done compacting them).
 size_t decode_attend_words(const Shape &s) {
     return (size_t)s.d + (size_t)DS_WAVES * (WAVE + 2 + 5 * s.d) + s.L + s.R;
 }
 size_t decode_route_words(const Shape &s) {
     const size_t ac = (size_t)std::min(s.A, s.NB);
-    return (size_t)s.d + s.P * s.K + (s.A + 1) + 2 * (size_t)s.NB + std::max(2 * ac, (size_t)s.NB);
+    return (size_t)s.d + s.P * s.K + (s.A + 1) + 3 * (size_t)s.NB + ac + 2;
 }
 size_t decode_step_lds(const Shape &s) { return (decode_attend_words(s) + decode_route_words(s)) * 4; }
 
@@ -211,7 +241,7 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
     const float *__restrict__ sin_t,
     const float *__restrict__ cb, const float *__restrict__ kbar,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ entries,
-    int32_t *__restrict__ sel, void *__restrict__ out) {
+    int32_t *__restrict__ sel, void *__restrict__ out, WalkPairs wp) {
     constexpr int H = D / 2, DS = D / P;
     constexpr int DPL = D / WAVE;                 // output dims per lane
     extern __shared__ __align__(16) float dstep_lds[];
@@ -229,11 +259,10 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
     int *off = reinterpret_cast<int *>(sc + P * K);      // [A + 1] list offsets
     int *ent = off + A + 1;                              // [NB] list entries
     int *pool_n = ent + NB;                              // [NB] pooled blocks
-    float *un = reinterpret_cast<float *>(pool_n + NB);
-    const int AC = min(A, NB);
-    int *cand = reinterpret_cast<int *>(un);             // [AC] extension addresses
-    float *sig = un + AC;                                // [AC] their sums
-    float *pool_r = un;                                  // [NB] rerank scores (after the extension)
+    float *pool_r = reinterpret_cast<float *>(pool_n + NB);   // [NB] rerank scores
+    int *cand = reinterpret_cast<int *>(pool_r + NB);    // [min(A, NB)] eligible addresses
+    int *ccount = cand + min(A, NB);                     // their number
+    int *hdone = ccount + 1;                             // waves done compacting them
 
     const int route = blockIdx.x;                        // b * Hq + h
     const int b = route / s.Hq, h = route % s.Hq, g = h / s.G;
@@ -298,6 +327,10 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
         }
     }
     for (int j = tid; j < nloc; j += DS_THREADS) blk[j] = lo + j;
+    if (tid == 0) {
+        *ccount = 0;
+        *hdone = 0;
+    }
     __syncthreads();
 
     // ---- attention state of this wave, and one 64-key item
@@ -510,6 +543,46 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
     };
 
     int *blk_rem = blk + nloc;                    // [R] the selection, for the attention
+    // The addresses whose list holds an eligible block (its first entry, the
+    // smallest, at most last), as codes c0 | c1 << 16 in cand, in no set
+    // order: the walk past its first M addresses visits only those (below).
+    // They do not depend on the query, so the waves without a local block
+    // collect them while wave 0 scores and sorts (addresses first + lane,
+    // step stride); with no such wave, wave 0 collects them when it needs them.
+    const int last = qb - s.L;
+    const int nhelp = max(0, DS_WAVES - 1 - nloc_items);
+    auto compact = [&](int first, int stride) {
+        const int AC = min(A, NB);
+        int c0 = P == 1 ? first + lane : (first + lane) / K, c1 = P == 1 ? 0 : (first + lane) % K;
+        const int s0 = P == 1 ? stride : stride / K, s1 = P == 1 ? 0 : stride % K;
+        constexpr int CB = 4;                     // steps whose reads are in flight together
+        for (int a0 = first; a0 < A; a0 += CB * stride) {
+            int e0[CB], e1[CB], f[CB], cc[CB];
+#pragma unroll
+            for (int v = 0; v < CB; ++v) {
+                const int ac = min(a0 + v * stride + lane, A - 1);
+                e0[v] = off[ac];
+                e1[v] = off[ac + 1];
+                cc[v] = c0 | c1 << 16;
+                c0 += s0;
+                c1 += s1;
+                if (P == 2 && c1 >= K) { c1 -= K; ++c0; }
+            }
+#pragma unroll
+            for (int v = 0; v < CB; ++v) f[v] = e0[v] < e1[v] ? ent[e0[v]] : INT_MAX;
+#pragma unroll
+            for (int v = 0; v < CB; ++v) {
+                const bool ok = a0 + v * stride + lane < A && f[v] <= last;
+                const uint64_t msk = __ballot(ok);
+                if (msk) {
+                    int at = 0;
+                    if (lane == 0) at = atomicAdd(ccount, __popcll(msk));
+                    at = __builtin_amdgcn_readlane(at, 0) + __popcll(msk & lanemask);
+                    if (ok && at < AC) cand[at] = cc[v];   // a valid index has at most AC such lists
+                }
+            }
+        }
+    };
     if (wave == 0) {
         if (!search) {   // bypass: every eligible block, in order
             for (int r = lane; r < R; r += WAVE) {
@@ -537,7 +610,6 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
-            const int last = qb - s.L;
             int npool = 0;
             // the eligible prefix of list a joins the pool
             auto take = [&](int a) {
@@ -607,6 +679,11 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
             // sorted (one wave sort), then those pairs, and the first n_probes
             // are the walk's.
             const int np1 = min(A, s.npr);
+            // The sort gives the walk's first M >= np1 addresses in order: for
+            // P = 2 the largest M (at most np1 + 16) whose pairs fit the wave
+            // (19 for 8 probes; every pair rule above holds for M as for
+            // n_probes), for P = 1 every code (wp, made on the host).
+            const int M = wp.M;
             uint64_t wk;                             // lane r: key of the r-th visited address
             if constexpr (P == 1) {
                 wk = sort_desc<64>(lane < K ? order_key(sc[lane], lane) : 0ull, lane);
@@ -622,14 +699,8 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                     k1 = sort_desc<64>(lane < K ? order_key(sc[K + lane], lane) : 0ull, lane);
                 }
                 // lane -> its pair (x, y), x-major
-                int rem = lane, px = -1, py = 0;
-                for (int x = 0; x < min(s.npr, K); ++x) {
-                    const int cnt = min(s.npr / (x + 1), K);
-                    if (px < 0) {
-                        if (rem < cnt) { px = x; py = rem; }
-                        else rem -= cnt;
-                    }
-                }
+                const int xy = wp.xy[lane];
+                const int px = xy == 0xFFFF ? -1 : (xy & 0xFF), py = xy == 0xFFFF ? 0 : xy >> 8;
                 const uint64_t kx = shfl_u64(k0, max(px, 0)), ky = shfl_u64(k1, py);
                 const int c0 = key_id(kx), c1 = key_id(ky);
                 const bool ok = px >= 0 && kx != 0ull && ky != 0ull;
@@ -639,7 +710,7 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                 wk = npairs <= 32 ? sort_desc<32>(pk, lane) : sort_desc<64>(pk, lane);
             }
             take_lists(lane < np1 ? key_id(wk) : -1, 0);
-            const uint64_t prev = shfl_u64(wk, np1 - 1);   // key of the last visited address
+            uint64_t prev = shfl_u64(wk, np1 - 1);         // key of the last visited address
             const int npool1 = npool;
             const float *kb = kbar + u * (size_t)NB * D;
             // the summary rows of the first 64 pooled blocks (their first 64
@@ -654,50 +725,38 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
 #pragma unroll
                 for (int j = 0; j < KPW; ++j) kpre[j] = kr[j];
             }
-            // Phase 2: after the n_probes best only addresses whose list has an
-            // eligible block can change the pool or end the walk; they are
-            // walked alone (at most R more rounds, each by a wave arg-max over
-            // them; candidate x holds its address in cand[x] and its sum in
-            // sig[x]).
-            if (npool < R && np1 < A) {
-                int ncand = 0;
-                // lane's address a0 + lane as codes (c0, c1), advanced by 64 per step
-                int c0 = P == 1 ? lane : lane / K, c1 = P == 1 ? 0 : lane % K;
-                const int s0 = P == 1 ? WAVE : WAVE / K, s1 = P == 1 ? 0 : WAVE % K;
-                // SB steps at a time: their list offsets and sums are read
-                // together, then their lists' first entries
-                constexpr int SB = 8;
-                for (int a0 = 0; a0 < A; a0 += SB * WAVE) {
-                    int e0[SB], e1[SB], f[SB];
-                    float sa[SB];
-#pragma unroll
-                    for (int u = 0; u < SB; ++u) {
-                        const int a = a0 + u * WAVE + lane;
-                        const int ac = min(a, A - 1);
-                        e0[u] = off[ac];
-                        e1[u] = off[ac + 1];
-                        sa[u] = a < A ? sigma(c0, c1) : 0.0f;
-                        c0 += s0;
-                        c1 += s1;
-                        if (P == 2 && c1 >= K) { c1 -= K; ++c0; }
-                    }
-#pragma unroll
-                    for (int u = 0; u < SB; ++u) f[u] = e0[u] < e1[u] ? ent[e0[u]] : INT_MAX;
-#pragma unroll
-                    for (int u = 0; u < SB; ++u) {
-                        const int a = a0 + u * WAVE + lane;
-                        const bool ok = a < A && f[u] <= last && order_key(sa[u], a) < prev;
-                        const uint64_t msk = __ballot(ok);
-                        if (ok) {
-                            const int x = ncand + __popcll(msk & lanemask);
-                            cand[x] = a;
-                            sig[x] = sa[u];
-                        }
-                        ncand += __popcll(msk);
-                    }
+            // Phase 2 begins with the walk's next addresses, ranks np1 .. M-1,
+            // already in order: their lists are taken up to the one that
+            // brings the pool to R.  Past rank M only addresses whose list
+            // has an eligible block can change the pool or end the walk; they
+            // are walked alone (at most R more picks, each by a wave arg-max
+            // over the collected addresses the walk has not visited).
+            if (npool < R && np1 < M) {
+                const int nx = M - np1;
+                // every lane takes part in the exchange (a lane exchange reads 0
+                // from a lane that is not active in it)
+                const uint64_t kn = shfl_u64(wk, min(lane + np1, WAVE - 1));
+                take_lists(lane < nx ? key_id(kn) : -1, R - npool);
+                prev = shfl_u64(wk, M - 1);
+            }
+            if (npool < R && M < A) {
+                if (nhelp == 0) {
+                    compact(0, WAVE);
+                } else {
+                    // the helper waves end their compaction without waiting
+                    // on anything, so this wait ends
+                    while (__hip_atomic_load(hdone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < nhelp)
+                        __builtin_amdgcn_s_sleep(1);
                 }
                 __builtin_amdgcn_s_waitcnt(0xc07f);
                 __builtin_amdgcn_wave_barrier();
+                const int ncand = min(*ccount, min(A, NB));
+                // candidate x's key, or 0 for an address the walk has visited
+                auto cand_key = [&](int x) {
+                    const int cc = cand[x], c0 = cc & 0xFFFF, c1 = cc >> 16;
+                    const uint64_t k = order_key(sigma(c0, c1), P == 1 ? c0 : c0 * K + c1);
+                    return k < prev ? k : 0ull;
+                };
                 // rounds: with at most NKR candidates per lane their keys stay
                 // in registers (a taken key is cleared; keys are distinct)
                 constexpr int NKR = 8;
@@ -706,7 +765,7 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
 #pragma unroll
                     for (int t = 0; t < NKR; ++t) {
                         const int x = lane + t * WAVE;
-                        ck[t] = x < ncand ? order_key(sig[x], cand[x]) : 0ull;
+                        ck[t] = x < ncand ? cand_key(x) : 0ull;
                     }
                     // every candidate list holds an eligible block, so the
                     // walk ends within the R - npool best: pick them in
@@ -729,7 +788,7 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                     while (npool < R) {
                         uint64_t best = 0;
                         for (int x = lane; x < ncand; x += WAVE) {
-                            const uint64_t k = order_key(sig[x], cand[x]);
+                            const uint64_t k = cand_key(x);
                             if (k < pv) best = key_max(best, k);
                         }
                         best = wave_max_key(best);
@@ -804,10 +863,14 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
                 blk_rem[r] = -1;
             }
         }
-    } else {
+    } else if (wave - 1 < nloc_items) {
         // the local blocks, while wave 0 routes
         for (int it = wave - 1; it < nloc_items; it += DS_WAVES - 1)
             attend_item(it, std::false_type{});
+    } else if (search) {
+        compact((wave - 1 - nloc_items) * WAVE, nhelp * WAVE);
+        __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): its candidates written
+        if (lane == 0) __hip_atomic_fetch_add(hdone, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
     // the selected blocks, on every wave
@@ -862,7 +925,7 @@ hipError_t run_decode(const Shape &s, int pos, const void *q, const void *kc, co
     const hipError_t e = lds_at_least(fn, lds);
     if (e != hipSuccess) return e;
     fn<<<routes, DS_THREADS, lds, st>>>(s, pos, q, kc, vc, krot, cos_t, sin_t, cb, kbar, offsets,
-                                        entries, sel, out);
+                                        entries, sel, out, walk_pairs(s));
     return hipGetLastError();
 }
 
