@@ -872,13 +872,15 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
 
     // Merge inputs of this lane's query for the first RP slots, one tile
     // ahead: entry positions are fetched when the previous tile starts, the
-    // log-sum-exps and partial rows when its attention is done.  (Prep
-    // leaves every slot of a uniform tile at -1, so no tile flag is needed.)
+    // log-sum-exps and partial rows when its output is stored, so they land
+    // during this tile's attention; the merge reads them where they were
+    // loaded (lse_n, o_n).  (Prep leaves every slot of a uniform tile at -1,
+    // so no tile flag is needed.)
     constexpr int RP = 2;
     constexpr int RX = 6;   // further slots merged from registers (R <= RP + RX)
     int ep_c[RP], ep_n[RP];
-    float lse_c[RP], lse_n[RP];
-    PartChunks<D, BF16> o_c[RP], o_n[RP];
+    float lse_n[RP];
+    PartChunks<D, BF16> o_n[RP];
     auto fetch_ep = [&](int it) {
         const long rt = it < i_end ? (long)(it / ntt) * s.T + (ntt - 1 - it % ntt) * 64 +
                                          wave * 16 + lr
@@ -896,12 +898,15 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
     };
     auto advance = [&]() {
 #pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            ep_c[r] = ep_n[r];
-            lse_c[r] = lse_n[r];
-            o_c[r] = o_n[r];
-        }
+        for (int r = 0; r < RP; ++r) ep_c[r] = ep_n[r];
     };
+    // this lane's query row of tile `it`, issued one tile ahead
+    auto q_at = [&](int it) {
+        const int bh_ = it / ntt, tt_ = ntt - 1 - it % ntt;
+        return (((size_t)(bh_ / s.Hq) * s.T + tt_ * 64 + wave * 16 + lr) * s.Hq + bh_ % s.Hq) * D;
+    };
+    QFrags<D, BF16> qst, qst_n;
+    qst_n.issue(q_rot, i_beg < i_end ? q_at(i_beg) : 0, i_beg < i_end);
     fetch_ep(i_beg);
     fetch_part();
     advance();
@@ -917,8 +922,8 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
     const long route0 = (long)bh * T_ + t0;
 
     const int tq = t0 + wave * 16 + lr;  // this lane's query position
-    QFrags<D, BF16> qst;
-    qst.issue(q_rot, (((size_t)b * T_ + tq) * Hq + h) * D, true);
+    qst = qst_n;                          // landed during the previous tile
+    qst_n.issue(q_rot, item + 1 < i_end ? q_at(item + 1) : 0, item + 1 < i_end);
     const long route = route0 + wave * 16 + lr;
     fetch_ep(item + 1);   // the next tile's entry positions, in flight
     if (uni) {  // shared remote blocks of the tile: valid first occurrences of row 0
@@ -1002,8 +1007,6 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
         kb_cur = kb_next;
     }
 
-    fetch_part();   // the next tile's partial states, in flight during the merge
-
     // merge: local (and shared) part, then the remote partials in slot order
     const float lse = m + __builtin_amdgcn_logf(l);
     const float inv = 1.0f / l;
@@ -1027,7 +1030,7 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
         float M = lse;
 #pragma unroll
         for (int r = 0; r < RP; ++r)
-            if (r < R && ep_c[r] >= 0) M = fmaxf(M, lse_c[r]);
+            if (r < R && ep_c[r] >= 0) M = fmaxf(M, lse_n[r]);
 #pragma unroll
         for (int x = 0; x < RX; ++x)
             if (ex[x] >= 0) M = fmaxf(M, lx[x]);
@@ -1039,10 +1042,10 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
 #pragma unroll
         for (int r = 0; r < RP; ++r) {   // prefetched slots (static indexes)
             if (r >= R || ep_c[r] < 0) continue;
-            const float w = __builtin_amdgcn_exp2f(lse_c[r] - M);
+            const float w = __builtin_amdgcn_exp2f(lse_n[r] - M);
             wsum += w;
             float x[D / 16][4];
-            o_c[r].unpack(x);
+            o_n[r].unpack(x);
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
@@ -1076,7 +1079,7 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
     } else if (!uni) {
         const int32_t *ep = entry_pos + route * R;
         auto ep_at = [&](int r) { return r < RP ? ep_c[r] : ep[r]; };
-        auto lse_at = [&](int r) { return r < RP ? lse_c[r] : part_lse[ep[r]]; };
+        auto lse_at = [&](int r) { return r < RP ? lse_n[r] : part_lse[ep[r]]; };
         float M = lse;
         for (int r = 0; r < R; ++r)
             if (ep_at(r) >= 0) M = fmaxf(M, lse_at(r));
@@ -1088,10 +1091,10 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
 #pragma unroll
         for (int r = 0; r < RP; ++r) {   // prefetched slots (static indexes)
             if (r >= R || ep_c[r] < 0) continue;
-            const float w = __builtin_amdgcn_exp2f(lse_c[r] - M);
+            const float w = __builtin_amdgcn_exp2f(lse_n[r] - M);
             wsum += w;
             float x[D / 16][4];
-            o_c[r].unpack(x);
+            o_n[r].unpack(x);
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
@@ -1137,6 +1140,7 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
                 *reinterpret_cast<const u32x4 *>(stg + rr * OS + d0);
         }
     }
+    fetch_part();   // the next tile's partial states, in flight during its attention
     advance();
     }
 }
