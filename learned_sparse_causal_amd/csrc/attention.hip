@@ -614,11 +614,16 @@ __device__ __forceinline__ int bin_start_of(const int32_t *bin_local, const int3
 // the separate scan's result: at most this many (16 KB of LDS).
 constexpr int SCATTER_SCAN_MAX = 2048;
 
+// (query, slot) entries per scatter thread: their first loads are issued
+// before the workgroup-total scan, and the grid is a quarter as large.
+constexpr int SCATTER_EPT = 4;
+
 // Scatter (query, slot) ids into bin order and replace each entry's rank by
 // its list position (where its partial state will be written); threads
 // below nbins also write their bin's entries of the chunk table.  With
 // SCAN, every workgroup first forms the exclusive scan of the binsum
 // workgroup totals (wg_sum, nwg pairs) in LDS; else wg_sum already holds it.
+// Thread t of workgroup w takes entries (w SCATTER_EPT + k) 256 + t.
 template <bool SCAN>
 __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbins,
                                                       const int32_t *__restrict__ sel,
@@ -633,6 +638,16 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     __shared__ int32_t base_s[SCAN ? 2 * SCATTER_SCAN_MAX + 2 : 1];
     const int32_t *wg_base = wg_sum;
+    // this thread's entries: ranks and selections, in flight during the scan
+    const long n = (long)s.B * s.Hq * s.T * s.R;
+    const long e0 = (long)blockIdx.x * SCATTER_EPT * 256 + threadIdx.x;
+    int pos[SCATTER_EPT], sl[SCATTER_EPT];
+#pragma unroll
+    for (int k = 0; k < SCATTER_EPT; ++k) {
+        const long e = e0 + k * 256;
+        pos[k] = e < n ? entry_pos[e] : -1;
+        sl[k] = e < n ? sel[e] : 0;
+    }
     if constexpr (SCAN) {
         // thread t owns totals [t * per, t * per + per); a workgroup scan of
         // its sums places them (same arithmetic as k_attn_scan)
@@ -701,18 +716,28 @@ __global__ __launch_bounds__(256) void k_attn_scatter(Shape s, int nseg, int nbi
             if (c == nchunks - 1) wg_first[grid_r] = (int)nchunks;
         }
     }
-    const long n = (long)s.B * s.Hq * s.T * s.R;
-    if (i >= n) return;
-    const int pos = entry_pos[i];
-    if (pos < 0) return;
-    const long route = i / s.R;
-    const int t = (int)(route % s.T);
-    const int h = (int)((route / s.T) % s.Hq), b = (int)(route / ((long)s.T * s.Hq));
-    const long bin = ((long)b * s.Hkv + h / s.G) * s.NB + sel[i];
-    const long sr = ((bin / s.NB) * nseg + t / SEG) * (long)s.NB + bin % s.NB;
-    const int at = bin_start_of(bin_local, wg_base, bin) + seg_rel[sr] + pos;
-    list_q[at] = (int32_t)(((long)b * s.T + t) * s.Hq + h);   // row of q_rot
-    entry_pos[i] = at;                                         // where its partial will be
+    // every entry's bin start and segment offset in one batch, then the writes
+    int bl[SCATTER_EPT], sg[SCATTER_EPT], qrow[SCATTER_EPT];
+    long bin[SCATTER_EPT];
+#pragma unroll
+    for (int k = 0; k < SCATTER_EPT; ++k) {
+        const long e = e0 + k * 256;
+        const long route = (pos[k] >= 0 ? e : 0) / s.R;
+        const int t = (int)(route % s.T);
+        const int h = (int)((route / s.T) % s.Hq), b = (int)(route / ((long)s.T * s.Hq));
+        bin[k] = ((long)b * s.Hkv + h / s.G) * s.NB + (pos[k] >= 0 ? sl[k] : 0);
+        const long sr = ((bin[k] / s.NB) * nseg + t / SEG) * (long)s.NB + bin[k] % s.NB;
+        bl[k] = bin_local[bin[k]];
+        sg[k] = seg_rel[sr];
+        qrow[k] = (int32_t)(((long)b * s.T + t) * s.Hq + h);   // row of q_rot
+    }
+#pragma unroll
+    for (int k = 0; k < SCATTER_EPT; ++k) {
+        if (pos[k] < 0) continue;
+        const int at = wg_base[2 * (bin[k] / BIN_WG)] + bl[k] + sg[k] + pos[k];
+        list_q[at] = qrow[k];
+        entry_pos[e0 + k * 256] = at;                            // where its partial will be
+    }
 }
 
 // Persistent over a contiguous range of chunks.  Every wave walks its tasks
@@ -1481,7 +1506,8 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     if (err != hipSuccess) return err;
     const unsigned grid_r = std::min<unsigned>(
         persistent_grid(k_attn_remote<D, BETA, BF16>, lds_r, max_chunks(s)), MAX_REMOTE_GRID);
-    const long nscat = std::max<long>(nent, nbins);
+    // threads: one per SCATTER_EPT entries, and at least one per bin
+    const long nscat = std::max<long>((nent + SCATTER_EPT - 1) / SCATTER_EPT, nbins);
     auto *scatter = scan_in_scatter ? k_attn_scatter<true> : k_attn_scatter<false>;
     scatter<<<dim3((unsigned)((nscat + 255) / 256)), 256, 0, st>>>(
         s, nseg, nbins, sel, w.entry_pos, w.bin_local, w.chunk_local, w.wg_sum, w.seg_rel,
