@@ -118,6 +118,38 @@ struct PartChunks {
 #pragma unroll
         for (int j = 0; j < NCH; ++j) c[j] = u32x4{0u, 0u, 0u, 0u};
     }
+    // The row's log-sum-exp rides in the row itself, so the merge reads one
+    // line per partial: byte lg of its 32 bits goes in the lowest mantissa
+    // bits of chunk 0 of lane group lg (bf16: the last bit of each of its 8
+    // elements, at most one unit in the last place each; fp32: the last two
+    // bits of each of its 4).
+    __device__ __forceinline__ void embed(float lse, int lg) {
+        const uint32_t b = (__float_as_uint(lse) >> (8 * lg)) & 0xFFu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (BF16)
+                c[0][k] = (c[0][k] & 0xFFFEFFFEu) | ((b >> (2 * k)) & 1u) | (((b >> (2 * k + 1)) & 1u) << 16);
+            else
+                c[0][k] = (c[0][k] & ~3u) | ((b >> (2 * k)) & 3u);
+        }
+    }
+    // The log-sum-exp of the row a lane group holds; every lane of the
+    // wave must take part (the bytes are exchanged between the row's lanes
+    // lane, lane ^ 16, lane ^ 32 and lane ^ 48).
+    __device__ __forceinline__ float lse(int lg) const {
+        uint32_t b = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (BF16)
+                b |= ((c[0][k] & 1u) << (2 * k)) | (((c[0][k] >> 16) & 1u) << (2 * k + 1));
+            else
+                b |= (c[0][k] & 3u) << (2 * k);
+        }
+        uint32_t w = b << (8 * lg);
+        w |= (uint32_t)__shfl_xor((int)w, 16);
+        w |= (uint32_t)__shfl_xor((int)w, 32);
+        return __uint_as_float(w);
+    }
 };
 
 __device__ __forceinline__ void store4(u16 *p, const float *x) {
@@ -753,8 +785,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
 void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
                    const Elem<BF16> *__restrict__ k_rot, const Elem<BF16> *__restrict__ v,
                    const int32_t *__restrict__ list_q, const int4 *__restrict__ chunk_desc,
-                   const int32_t *__restrict__ wg_first, float *__restrict__ part_lse,
-                   Elem<BF16> *__restrict__ part_o) {
+                   const int32_t *__restrict__ wg_first, Elem<BF16> *__restrict__ part_o) {
     using T = Tile<D, BF16>;
     using E = Elem<BF16>;
     constexpr int NSUB = BETA / 64;
@@ -837,7 +868,6 @@ void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
                     attend64<D, BF16, false, false>(qf, Ks + T::K_ELEMS, Vts + T::V_ELEMS, 0, 0, o,
                                                     m, l);
                 if (row_now >= 0) {
-                    if (lg == 0) part_lse[row_now] = m + __builtin_amdgcn_logf(l);
                     const float inv = 1.0f / l;
                     float x[D / 16][4];
 #pragma unroll
@@ -846,6 +876,7 @@ void k_attn_remote(Shape s, const Elem<BF16> *__restrict__ q_rot,
                         for (int r = 0; r < 4; ++r) x[dt][r] = o[dt][r] * inv;
                     PartChunks<D, BF16> pc;
                     pc.pack(x);
+                    pc.embed(m + __builtin_amdgcn_logf(l), lg);   // base-2 log-sum-exp
                     pc.store(part_o + (size_t)row_now * D, lg);
                 }
             }
@@ -872,7 +903,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF16 ? 2 : 
 void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
                   const Elem<BF16> *__restrict__ k_rot, const Elem<BF16> *__restrict__ v,
                   const int32_t *__restrict__ sel, const int32_t *__restrict__ tile_flag,
-                  const int32_t *__restrict__ entry_pos, const float *__restrict__ part_lse,
+                  const int32_t *__restrict__ entry_pos,
                   const Elem<BF16> *__restrict__ part_o, Elem<BF16> *__restrict__ out) {
     using T = Tile<D, BF16>;
     using E = Elem<BF16>;
@@ -897,14 +928,13 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
 
     // Merge inputs of this lane's query for the first RP slots, one tile
     // ahead: entry positions are fetched when the previous tile starts, the
-    // log-sum-exps and partial rows when its output is stored, so they land
-    // during this tile's attention; the merge reads them where they were
-    // loaded (lse_n, o_n).  (Prep leaves every slot of a uniform tile at -1,
-    // so no tile flag is needed.)
+    // partial rows (which carry their log-sum-exps) when its output is
+    // stored, so they land during this tile's attention; the merge reads them
+    // where they were loaded (o_n).  (Prep leaves every slot of a uniform
+    // tile at -1, so no tile flag is needed.)
     constexpr int RP = 2;
-    constexpr int RX = 6;   // further slots merged from registers (R <= RP + RX)
+    constexpr int RX = 6;   // further slots merged two rows at a time (R <= RP + RX)
     int ep_c[RP], ep_n[RP];
-    float lse_n[RP];
     PartChunks<D, BF16> o_n[RP];
     auto fetch_ep = [&](int it) {
         const long rt = it < i_end ? (long)(it / ntt) * s.T + (ntt - 1 - it % ntt) * 64 +
@@ -916,7 +946,6 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
     auto fetch_part = [&]() {
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
-            lse_n[r] = ep_n[r] >= 0 ? part_lse[ep_n[r]] : 0.0f;
             if (ep_n[r] >= 0) o_n[r].load(part_o + (size_t)ep_n[r] * D, lg);
             else o_n[r].zero();
         }
@@ -1040,25 +1069,16 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[dt][r] = o[dt][r] * inv;
-    if (!uni && R > RP && R <= RP + RX) {
-        // slots RP .. R-1 come from global memory: their entry positions in
-        // one batch, then their log-sum-exps in one batch, then the partial
-        // rows two at a time (loads clamped to entry 0, weights of absent
-        // slots zero), accumulated in slot order
-        const int32_t *ep = entry_pos + route * R;
-        int ex[RX];
-        float lx[RX];
+    if (!uni) {
+        // the prefetched slots' log-sum-exps, from their rows (the exchange
+        // between a row's lanes runs before any per-lane branch)
+        float lse_p[RP];
 #pragma unroll
-        for (int x = 0; x < RX; ++x) ex[x] = RP + x < R ? ep[RP + x] : -1;
-#pragma unroll
-        for (int x = 0; x < RX; ++x) lx[x] = part_lse[max(ex[x], 0)];
+        for (int r = 0; r < RP; ++r) lse_p[r] = o_n[r].lse(lg);
         float M = lse;
 #pragma unroll
         for (int r = 0; r < RP; ++r)
-            if (r < R && ep_c[r] >= 0) M = fmaxf(M, lse_n[r]);
-#pragma unroll
-        for (int x = 0; x < RX; ++x)
-            if (ex[x] >= 0) M = fmaxf(M, lx[x]);
+            if (r < R && ep_c[r] >= 0) M = fmaxf(M, lse_p[r]);
         float wsum = __builtin_amdgcn_exp2f(lse - M);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
@@ -1067,7 +1087,7 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
 #pragma unroll
         for (int r = 0; r < RP; ++r) {   // prefetched slots (static indexes)
             if (r >= R || ep_c[r] < 0) continue;
-            const float w = __builtin_amdgcn_exp2f(lse_n[r] - M);
+            const float w = __builtin_amdgcn_exp2f(lse_p[r] - M);
             wsum += w;
             float x[D / 16][4];
             o_n[r].unpack(x);
@@ -1076,68 +1096,50 @@ void k_attn_local(Shape s, const Elem<BF16> *__restrict__ q_rot,
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
         }
-#pragma unroll
-        for (int x0 = 0; x0 < RX; x0 += 2) {
-            if (__ballot(ex[x0] >= 0 || (x0 + 1 < RX && ex[x0 + 1] >= 0)) == 0ull) continue;
-            PartChunks<D, BF16> pc[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-                if (x0 + u < RX) pc[u].load(part_o + (size_t)max(ex[x0 + u], 0) * D, lg);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                if (x0 + u >= RX || ex[x0 + u] < 0) continue;
-                const float w = __builtin_amdgcn_exp2f(lx[x0 + u] - M);
-                wsum += w;
-                float x[D / 16][4];
-                pc[u].unpack(x);
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
-            }
-        }
-        const float iw = 1.0f / wsum;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[dt][r] *= iw;
-    } else if (!uni) {
-        const int32_t *ep = entry_pos + route * R;
-        auto ep_at = [&](int r) { return r < RP ? ep_c[r] : ep[r]; };
-        auto lse_at = [&](int r) { return r < RP ? lse_n[r] : part_lse[ep[r]]; };
-        float M = lse;
-        for (int r = 0; r < R; ++r)
-            if (ep_at(r) >= 0) M = fmaxf(M, lse_at(r));
-        float wsum = __builtin_amdgcn_exp2f(lse - M);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[dt][r] *= wsum;
-#pragma unroll
-        for (int r = 0; r < RP; ++r) {   // prefetched slots (static indexes)
-            if (r >= R || ep_c[r] < 0) continue;
-            const float w = __builtin_amdgcn_exp2f(lse_n[r] - M);
-            wsum += w;
-            float x[D / 16][4];
-            o_n[r].unpack(x);
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
-        }
-        for (int r = RP; r < R; ++r) {
-            if (ep_at(r) < 0) continue;
-            const long e = ep_at(r);
-            const float w = __builtin_amdgcn_exp2f(lse_at(r) - M);
-            wsum += w;
-            PartChunks<D, BF16> pc;
-            pc.load(part_o + (size_t)e * D, lg);
+        // slots RP .. R-1, in slot order: their rows come from global memory
+        // (loads clamped to entry 0) and bring their log-sum-exps, so these
+        // merge online (the running maximum rises as needed; a slot that
+        // does not raise it rescales by exactly 1)
+        auto add_slot = [&](float lu, const PartChunks<D, BF16> &pc) {
+            const float Mn = fmaxf(M, lu);
+            const float sc = __builtin_amdgcn_exp2f(M - Mn), w = __builtin_amdgcn_exp2f(lu - Mn);
+            wsum = wsum * sc + w;
             float x[D / 16][4];
             pc.unpack(x);
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] += w * x[dt][rr];
+                for (int rr = 0; rr < 4; ++rr) acc[dt][rr] = acc[dt][rr] * sc + w * x[dt][rr];
+            M = Mn;
+        };
+        const int32_t *ep = entry_pos + route * R;
+        if (R > RP && R <= RP + RX) {
+            // entry positions in one batch, then the rows two at a time
+            int ex[RX];
+#pragma unroll
+            for (int x = 0; x < RX; ++x) ex[x] = RP + x < R ? ep[RP + x] : -1;
+#pragma unroll
+            for (int x0 = 0; x0 < RX; x0 += 2) {
+                if (__ballot(ex[x0] >= 0 || (x0 + 1 < RX && ex[x0 + 1] >= 0)) == 0ull) continue;
+                PartChunks<D, BF16> pc[2];
+                float lu[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    if (x0 + u < RX) pc[u].load(part_o + (size_t)max(ex[x0 + u], 0) * D, lg);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) lu[u] = x0 + u < RX ? pc[u].lse(lg) : 0.0f;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    if (x0 + u < RX && ex[x0 + u] >= 0) add_slot(lu[u], pc[u]);
+            }
+        } else {
+            for (int r = RP; r < R; ++r) {
+                const int e = ep[r];
+                PartChunks<D, BF16> pc;
+                pc.load(part_o + (size_t)max(e, 0) * D, lg);
+                const float lu = pc.lse(lg);
+                if (e >= 0) add_slot(lu, pc);
+            }
         }
         const float iw = 1.0f / wsum;
 #pragma unroll
@@ -1461,7 +1463,6 @@ struct AttnWs {
     int32_t *cnt, *seg_rel, *bin_local, *chunk_local, *wg_sum, *tile_flag, *entry_pos, *list_q,
         *wg_first;
     int4 *chunk_desc;
-    float *part_lse;
     void *part_o, *q_rot, *k_rot;
 };
 
@@ -1516,7 +1517,7 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     if (err != hipSuccess) return err;
     k_attn_remote<D, BETA, BF16><<<dim3(grid_r), 256, lds_r, st>>>(
         s, reinterpret_cast<const E *>(w.q_rot), reinterpret_cast<const E *>(w.k_rot),
-        reinterpret_cast<const E *>(v), w.list_q, w.chunk_desc, w.wg_first, w.part_lse,
+        reinterpret_cast<const E *>(v), w.list_q, w.chunk_desc, w.wg_first,
         reinterpret_cast<E *>(w.part_o));
     const size_t lds_l = (size_t)(T::K_ELEMS + T::V_ELEMS + 4 * 16 * (D + 16 / sizeof(E))) *
                              sizeof(E) + (size_t)s.R * sizeof(int);
@@ -1525,7 +1526,7 @@ hipError_t run_attention(const Shape &s, const void *q, const void *k, const voi
     const unsigned grid_l = persistent_grid(k_attn_local<D, BETA, BF16>, lds_l, ntiles);
     k_attn_local<D, BETA, BF16><<<dim3(grid_l), 256, lds_l, st>>>(
         s, reinterpret_cast<const E *>(w.q_rot), reinterpret_cast<const E *>(w.k_rot),
-        reinterpret_cast<const E *>(v), sel, w.tile_flag, w.entry_pos, w.part_lse,
+        reinterpret_cast<const E *>(v), sel, w.tile_flag, w.entry_pos,
         reinterpret_cast<const E *>(w.part_o), reinterpret_cast<E *>(out));
     return hipGetLastError();
 }
@@ -1595,7 +1596,7 @@ size_t attention_ws_layout(const Shape &s, size_t *off) {
     off[6] = p; p = al(p + ntiles * 4);                       // tile flags
     off[7] = p; p = al(p + nent * 4);                         // entry ranks
     off[8] = p; p = al(p + (size_t)(MAX_REMOTE_GRID + 1) * 4);   // remote work split
-    off[9] = p; p = al(p + nent * 4);                         // partial lse
+    off[9] = p;                                               // (none: partial rows carry their log-sum-exps)
     off[10] = p; p = al(p + nent * (size_t)s.d * esz);        // partial outputs
     off[11] = p; p = al(p + (size_t)s.B * s.T * s.Hq * s.d * esz);   // rotated q
     off[12] = p; p = al(p + (size_t)s.B * s.T * s.Hkv * s.d * esz);  // rotated k
@@ -1629,7 +1630,6 @@ hipError_t launch_attention(const Shape &s, const void *q, const void *k, const 
     w.chunk_desc = reinterpret_cast<int4 *>(base + off[5]);
     w.tile_flag = reinterpret_cast<int32_t *>(base + off[6]);
     w.entry_pos = reinterpret_cast<int32_t *>(base + off[7]);
-    w.part_lse = reinterpret_cast<float *>(base + off[9]);
     w.part_o = base + off[10];
     w.q_rot = base + off[11];
     w.k_rot = base + off[12];
