@@ -139,12 +139,21 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
     const int dummy = PK * SROW * 4;                             // byte offset of a -inf row
 
     // Work items: (token group, batch, q-head) with the q-heads fastest and
-    // the latest token groups (the longest extension scans) first.  Workgroups
-    // are dealt to the XCDs round-robin, so every XCD gets a mix of heavy and
-    // light groups, and the heads of one token group run at about the same
-    // time and share its rotary-table rows in the caches.
+    // the latest token groups (the longest extension scans) first.  The
+    // workgroups are dealt to the 8 XCDs round-robin (workgroup i is the
+    // (i / 8)-th on XCD i % 8), and the items are placed for that: the token
+    // groups go to the XCDs in rank order (rank k on XCD k % 8), so every XCD
+    // gets heavy and light groups alike, and each XCD runs all batches and
+    // q-heads of its group together, so that they share the group's
+    // rotary-table rows in that XCD's L2 (dealt item by item, every XCD would
+    // fetch every group's rows).  With a group count that is not a multiple
+    // of 8 the items run in plain order.
     const int ngrp = (s.T + nw * WAVE - 1) / (nw * WAVE);
-    const int item = blockIdx.x;
+    const int per_grp = s.Hq * s.B;
+    const int item = ngrp % 8 == 0
+        ? ((int)(blockIdx.x / 8) / per_grp * 8 + (int)(blockIdx.x % 8)) * per_grp +
+              (int)(blockIdx.x / 8) % per_grp
+        : (int)blockIdx.x;
     const int h = item % s.Hq, b = (item / s.Hq) % s.B, g = h / s.G;
     const size_t ug = (size_t)b * s.Hkv + g;
     const int tw0 = (ngrp - 1 - item / (s.Hq * s.B)) * nw * WAVE;   // first token of the workgroup
