@@ -264,7 +264,16 @@ __global__ __launch_bounds__(DS_THREADS) void k_decode_step(
     int *ccount = cand + min(A, NB);                     // their number
     int *hdone = ccount + 1;                             // waves done compacting them
 
-    const int route = blockIdx.x;                        // b * Hq + h
+    // route b * Hq + h.  Workgroups are dealt to the 8 XCDs round-robin
+    // (workgroup i is the (i / 8)-th on XCD i % 8); the (batch, kv-head)
+    // groups go to the XCDs in turn and the G heads of a group run on one
+    // XCD, so the blocks they share (the local ones, and the selected ones
+    // they have in common) come from memory once into that XCD's L2.  With
+    // a group count that is not a multiple of 8 the routes run in order.
+    const int ngq = s.B * s.Hkv;
+    const int route = ngq % 8 == 0
+        ? ((int)(blockIdx.x / 8) / s.G * 8 + (int)(blockIdx.x % 8)) * s.G + (int)(blockIdx.x / 8) % s.G
+        : (int)blockIdx.x;
     const int b = route / s.Hq, h = route % s.Hq, g = h / s.G;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
     const uint64_t lanemask = (1ull << lane) - 1ull;
