@@ -146,11 +146,16 @@ void k_route(Shape s, const void *__restrict__ q, const float *__restrict__ cos_
     // gets heavy and light groups alike, and each XCD runs all batches and
     // q-heads of its group together, so that they share the group's
     // rotary-table rows in that XCD's L2 (dealt item by item, every XCD would
-    // fetch every group's rows).  With a group count that is not a multiple
-    // of 8 the items run in plain order.
+    // fetch every group's rows).  Each XCD then reads the block summaries of
+    // every (batch, kv-head) in its reranks, so this placement is used only
+    // while they all fit in half an L2 (2 MiB; measured: on the batch-8
+    // 64K-token workload, 8 MiB of summaries, it made the router 30 %
+    // slower).  Otherwise, or with a group count that is not a multiple of
+    // 8, the items run in plain order (each XCD then sees a few kv-heads).
     const int ngrp = (s.T + nw * WAVE - 1) / (nw * WAVE);
     const int per_grp = s.Hq * s.B;
-    const int item = ngrp % 8 == 0
+    const bool by_xcd = ngrp % 8 == 0 && (size_t)s.B * s.Hkv * NB * D * sizeof(float) <= (2u << 20);
+    const int item = by_xcd
         ? ((int)(blockIdx.x / 8) / per_grp * 8 + (int)(blockIdx.x % 8)) * per_grp +
               (int)(blockIdx.x / 8) % per_grp
         : (int)blockIdx.x;
