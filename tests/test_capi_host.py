@@ -82,7 +82,9 @@ def test_workspace_sizes(lib):
         attn = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_ATTENTION)
         es = 2 if cfg.dtype == "bf16" else 4
         nent = cfg.B * cfg.Hq * cfg.T * cfg.R
-        assert attn >= nent * (cfg.d * es + 12)
+        # per (query, slot): its rank in its bin, its list row, and its
+        # partial row (which carries the row's log-sum-exp in its low bits)
+        assert attn >= nent * (cfg.d * es + 8)
         mix = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_MIXER)
         assert mix > attn
         cal = lib.mono_workspace_bytes(ctypes.byref(c), binding.WS_CALIBRATE)
